@@ -1,0 +1,168 @@
+"""Seeded 3D-grid video-token inputs for non-causal diffusion self-attention.
+
+Stand-in for the WAN 2.2 self-attention workload that the TensorRT-LLM pull
+request "Add SkipSoftmax sparse attention support for visual generation"
+benchmarks (section "Benchmark": 720x1280, 81 frames, sequence length about
+75K). No prompts, weights or datasets are used: the inputs are synthetic with
+the same shapes and a distance-decaying logit structure, so that the
+fraction of negligible KV tiles behaves like a video model's.
+
+Recipe (the pages fix none of the constants; each is a stated choice):
+
+* Token t of a sequence sits at grid point p = (f, r, c) of an F x Hg x Wg
+  latent grid, frame-major: t = (f * Hg + r) * Wg + c.
+* Per head, a locality length ell_h ~ U[2, 16] grid units and 8 frequency
+  vectors w_k ~ N(0, ell_h^-2 I_3).
+* phi(p) = A * [sin(w_1.p), cos(w_1.p), ..., sin(w_8.p), cos(w_8.p)] fills
+  dims 0..15; dims 16..D-1 are zero. E[q.k] then decays like
+  exp(-|dp|^2 / (2 ell^2)) with grid distance.
+* q = sigma * N(0, I_D) + phi(p), k = sigma * N(0, I_D) + phi(p), v ~ N(0, I_D).
+* A^2 = L * sqrt(D) / 8 with peak logit L = 40 nats: q.k / sqrt(D) reaches L
+  for a token against itself, large enough that the strictest thresholds
+  still skip roughly a third of the tiles, the floor the ModelOpt README
+  ("Known Issues") reports for real diffusion models.
+* numpy default_rng(seed); draws in a fixed order: ell for all heads, w for
+  all heads, then per sequence and per head: q-noise, k-noise, v.
+* Q/K/V are produced in fp32 and rounded to bf16 (round to nearest even);
+  both the GPU path and the oracle consume exactly those bf16 values.
+
+This module contains no attention arithmetic.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+PEAK_LOGIT_NATS = 40.0
+N_FREQ = 8  # 8 frequency vectors -> 16 sin/cos features
+
+
+@dataclasses.dataclass(frozen=True)
+class VideoTokenConfig:
+    """One synthetic workload: B sequences, each on its own (F, Hg, Wg) grid."""
+
+    name: str
+    grids: Tuple[Tuple[int, int, int], ...]
+    num_heads: int
+    head_dim: int
+    sigma: float
+    block: int
+    seed: int
+    ell_range: Tuple[float, float] = (2.0, 16.0)
+    peak_logit: float = PEAK_LOGIT_NATS
+
+    @property
+    def seq_lens(self) -> List[int]:
+        return [f * h * w for (f, h, w) in self.grids]
+
+    @property
+    def cu_seqlens(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.seq_lens)]).astype(np.int32)
+
+    @property
+    def total_tokens(self) -> int:
+        return int(sum(self.seq_lens))
+
+    def dense_flops(self) -> float:
+        """Dense-equivalent FLOP of one forward: sum_b 4 * S_b^2 * H * D."""
+        return float(sum(4.0 * s * s * self.num_heads * self.head_dim for s in self.seq_lens))
+
+
+# The five workloads: tiny (oracle-sized), WAN-5B-like, the WAN-14B 720p
+# headline, its calibration pass (same shape, its own seed), and a varlen
+# batch of 720p / 480p / 240p-sized sequences.
+CONFIGS: Dict[str, VideoTokenConfig] = {
+    "tiny": VideoTokenConfig("tiny", ((4, 16, 16),), 2, 64, 0.5, 64, seed=0),
+    "wan5b": VideoTokenConfig("wan5b", ((16, 32, 32),), 24, 128, 1.0, 128, seed=1),
+    "headline": VideoTokenConfig("headline", ((21, 45, 80),), 40, 128, 0.5, 128, seed=2),
+    "calib": VideoTokenConfig("calib", ((21, 45, 80),), 40, 128, 0.5, 128, seed=3),
+    "varlen": VideoTokenConfig(
+        "varlen", ((21, 45, 80), (21, 30, 52), (21, 15, 26)), 40, 128, 0.5, 128, seed=4
+    ),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (round to nearest, ties to even); return the raw uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact fp32 value of each bf16 bit pattern."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def grid_positions(grid: Sequence[int]) -> np.ndarray:
+    """(S, 3) float64 grid coordinates (f, r, c) in frame-major token order."""
+    f, h, w = grid
+    ff, rr, cc = np.meshgrid(np.arange(f), np.arange(h), np.arange(w), indexing="ij")
+    return np.stack([ff.ravel(), rr.ravel(), cc.ravel()], axis=1).astype(np.float64)
+
+
+def fourier_amplitude(head_dim: int, peak_logit: float = PEAK_LOGIT_NATS) -> float:
+    """A with 8 * A^2 / sqrt(D) = peak_logit (8 cos terms equal to 1 at zero distance)."""
+    return math.sqrt(peak_logit * math.sqrt(head_dim) / N_FREQ)
+
+
+def make_inputs(cfg: VideoTokenConfig, heads: Sequence[int] | None = None) -> Dict[str, np.ndarray]:
+    """Generate bf16 Q, K, V for `cfg` as uint16 bit arrays of shape [T, H, D].
+
+    `heads` restricts generation to a subset of heads (the others stay zero);
+    the random stream is still consumed in full order so every generated head
+    is identical to the full generation.
+    Returns dict(q, k, v: uint16 [T,H,D]; cu_seqlens: int32 [B+1]; ell: [H]).
+    """
+    rng = np.random.default_rng(cfg.seed)
+    H, D = cfg.num_heads, cfg.head_dim
+    lo, hi = cfg.ell_range
+    ell = rng.uniform(lo, hi, size=H)
+    omega = rng.standard_normal((H, N_FREQ, 3)) / ell[:, None, None]
+    amp = fourier_amplitude(D, cfg.peak_logit)
+    want = set(range(H)) if heads is None else set(int(h) for h in heads)
+
+    T = cfg.total_tokens
+    out = {name: np.zeros((T, H, D), dtype=np.uint16) for name in ("q", "k", "v")}
+    cu = cfg.cu_seqlens
+    for b, grid in enumerate(cfg.grids):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        S = s1 - s0
+        pos = grid_positions(grid)
+        for h in range(H):
+            qn = rng.standard_normal((S, D), dtype=np.float32)
+            kn = rng.standard_normal((S, D), dtype=np.float32)
+            vv = rng.standard_normal((S, D), dtype=np.float32)
+            if h not in want:
+                continue
+            phase = pos @ omega[h].T  # (S, 8)
+            feat = np.empty((S, 2 * N_FREQ), dtype=np.float64)
+            feat[:, 0::2] = np.sin(phase)
+            feat[:, 1::2] = np.cos(phase)
+            feat *= amp
+            q = cfg.sigma * qn
+            k = cfg.sigma * kn
+            q[:, : 2 * N_FREQ] += feat.astype(np.float32)
+            k[:, : 2 * N_FREQ] += feat.astype(np.float32)
+            out["q"][s0:s1, h, :] = f32_to_bf16_bits(q)
+            out["k"][s0:s1, h, :] = f32_to_bf16_bits(k)
+            out["v"][s0:s1, h, :] = f32_to_bf16_bits(vv)
+    out["cu_seqlens"] = cu
+    out["ell"] = ell
+    return out
+
+
+def make_random_inputs(seq_lens: Sequence[int], num_heads: int, head_dim: int, seed: int,
+                       scale: float = 1.0) -> Dict[str, np.ndarray]:
+    """Plain N(0, scale^2) bf16 Q/K/V for edge-case shapes (ragged lengths, empty sequences)."""
+    rng = np.random.default_rng(seed)
+    T = int(sum(seq_lens))
+    out = {}
+    for name in ("q", "k", "v"):
+        x = (scale * rng.standard_normal((T, num_heads, head_dim))).astype(np.float32)
+        out[name] = f32_to_bf16_bits(x)
+    out["cu_seqlens"] = np.concatenate([[0], np.cumsum(seq_lens)]).astype(np.int32)
+    return out
