@@ -1,0 +1,221 @@
+/*
+ * ssa.h -- skip-softmax (BLASST) sparse attention for MI355X (gfx950), C ABI.
+ *
+ * The library computes the non-causal self-attention forward of video
+ * diffusion transformers with KV-tile skipping, and the companion
+ * calibration pass that measures skip ratios at many thresholds at once.
+ *
+ * Method sources (web pages, cited by title and section):
+ *  [README]  ModelOpt diffusers sparsity README, "Skip-Softmax Sparse
+ *            Attention for Diffusion Models": introduction, "Threshold
+ *            Modes", "Known Issues".
+ *  [TRITON]  ModelOpt pull request "skip-softmax ... via dedicated Triton
+ *            kernels": "Changes / Triton kernels", "Kernel backends",
+ *            "Method", "Calibration", "Threshold modes".
+ *  [PR1166]  ModelOpt pull request #1166 "Add the Skip softmax for
+ *            diffusion": "Usage" (br = bc = 128, non-causal, threshold trials).
+ *  [TRTLLM]  TensorRT-LLM pull request "Add SkipSoftmax sparse attention
+ *            support for visual generation": "Use Cases", "Priority Order".
+ *  [DOCS]    TensorRT-LLM docs "VisualGen Sparse Attention (Beta)":
+ *            "Skip Softmax Attention", "User Configuration".
+ *
+ * Conventions shared by every entry point
+ *  - Every function returns an int status: 0 = SSA_OK, > 0 = a warning (the
+ *    outputs are valid), < 0 = an error (outputs untouched unless stated).
+ *    Nothing falls back silently to dense attention.
+ *  - Tensors are bf16, packed "varlen": token-major [T, H, D] with T the sum
+ *    of the B sequence lengths (the [B, S, H, D] -> varlen conversion of
+ *    [TRITON] "Kernel backends"). Element (token t, head h, dim d) sits at
+ *    t * stride_token + h * stride_head + d; D is contiguous. Base pointers
+ *    must be 16-byte aligned and both strides multiples of 8 elements.
+ *  - Device pointers are caller-owned device memory (e.g. torch CUDA/HIP
+ *    tensors). The library allocates no device memory and keeps no state
+ *    between calls; it is reentrant. GPU work is enqueued on `stream`
+ *    (a hipStream_t, NULL = the legacy default stream) and is asynchronous:
+ *    outputs are ready once the stream is synchronized. Kernel-launch
+ *    failures are reported as SSA_ERR_HIP.
+ *  - Calls that overlap on the same output buffers race; the caller orders them.
+ */
+#ifndef SSA_H_
+#define SSA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define SSA_OK                   0
+#define SSA_WARN_EXTRAPOLATED    1  /* target sparsity outside the calibrated range */
+#define SSA_ERR_INVALID_ARG     -1  /* null pointer, bad shape/stride/alignment, NaN */
+#define SSA_ERR_UNSUPPORTED     -2  /* head_dim or block not built, too many heads */
+#define SSA_ERR_THRESHOLD_RANGE -3  /* resolved lambda outside [0, 1] */
+#define SSA_ERR_NO_FORMULA      -4  /* target sparsity requested without a formula */
+#define SSA_ERR_FIT_DEGENERATE  -5  /* fewer than two distinct usable sparsities */
+#define SSA_ERR_HIP             -6  /* HIP runtime / kernel launch failure */
+
+typedef void* ssa_stream_t; /* hipStream_t */
+
+/* ---- problem description ----------------------------------------------- */
+/* Self-attention over B packed sequences: q, k and v share cu_seqlens
+ * (S_q = S_k per sequence). Non-causal only ([PR1166] "Usage": is_causal
+ * False). The tile size block = Br = Bc is part of the method's definition,
+ * because skip decisions are taken per Br x Bc tile ([PR1166] "Usage":
+ * br = bc = 128). */
+typedef struct ssa_problem {
+  int32_t batch;             /* B >= 1 sequences                                  */
+  int32_t num_heads;         /* H in [1, 512]                                     */
+  int32_t head_dim;          /* D in {64, 128}                                    */
+  int32_t block;             /* Br = Bc in {64, 128}                              */
+  const int32_t* cu_seqlens; /* HOST array [B + 1]: cu[0] = 0, non-decreasing;
+                                sequence b is tokens [cu[b], cu[b+1]); empty
+                                sequences are allowed                              */
+  int64_t stride_token;      /* elements between tokens, same for q, k, v, o       */
+  int64_t stride_head;       /* elements between heads, same for q, k, v, o        */
+  double sm_scale;           /* softmax scale; 0 selects 1 / sqrt(D)               */
+} ssa_problem;
+
+/* ---- thresholds for the forward ---------------------------------------- */
+/* How the per-(sequence, head) threshold reaches the kernel ([README]
+ * "Threshold Modes"; [TRITON] "Threshold modes"):
+ *   SSA_THRESH_LAMBDA       value = lambda in [0, 1]; kernel compares against
+ *                           log2(lambda). lambda = 0 is dense (nothing skipped).
+ *   SSA_THRESH_LOG2         value = log2(lambda) passed through unchanged
+ *                           ("raw" threshold); -inf is dense; must be <= 0.
+ *   SSA_THRESH_SCALE_FACTOR value = scale factor sf; lambda = sf / S_b with S_b
+ *                           the key length of sequence b ([README] "Threshold
+ *                           Modes", calibrated row). sf = 0 is dense.
+ * A resolved lambda outside [0, 1] (or NaN) is SSA_ERR_THRESHOLD_RANGE. */
+#define SSA_THRESH_LAMBDA       0
+#define SSA_THRESH_LOG2         1
+#define SSA_THRESH_SCALE_FACTOR 2
+
+typedef struct ssa_thresholds {
+  int32_t kind;          /* SSA_THRESH_*                                         */
+  int32_t count;         /* 1 (same for all heads) or H (one value per head)     */
+  const double* values;  /* HOST array of `count` values                          */
+} ssa_thresholds;
+
+/* ---- the forward ------------------------------------------------------- */
+/* Skip-softmax FlashAttention forward ([TRITON] "Triton kernels", the forward
+ * kernel; [README] introduction). For each sequence b, head h and Q-block i
+ * (rows i*block .. i*block+block-1), KV tiles j = 0, 1, ... are visited in
+ * ascending order. With s = (q . k) * sm_scale * log2(e), rowmax_r the tile's
+ * maximum score in row r and m_r the running maximum before the tile,
+ * d = max over the block's valid rows of (rowmax_r - m_r); the tile is
+ * skipped when d < log2(lambda): its V is not loaded, no exponential and no
+ * P.V is computed, and the running statistics are left unchanged. Kept tiles
+ * update the online softmax as in FlashAttention. The first tile is never
+ * skipped. Scores are accumulated in fp32 from bf16 inputs, P is rounded to
+ * bf16 for the P.V product, O is rounded to bf16.
+ *
+ *  q, k, v    device, bf16 [T, H, D] (see conventions)
+ *  o          device, bf16 [T, H, D], written for every valid token
+ *  th         host, thresholds (see above)
+ *  skipped_bh device uint64 [B * H] or NULL: skipped KV tiles per (b, h)
+ *  total_bh   device uint64 [B * H] or NULL: visited KV tiles per (b, h)
+ *             (both are overwritten, not accumulated: the library zeroes them)
+ *  tile_mask  device uint8 [B, H, nq_max, nk_max] or NULL (debug): 0 = tile
+ *             kept, 1 = skipped, 2 = no such tile; dims from ssa_tile_mask_dims.
+ * Errors: SSA_ERR_INVALID_ARG, SSA_ERR_UNSUPPORTED, SSA_ERR_THRESHOLD_RANGE,
+ * SSA_ERR_HIP. */
+int ssa_attn_fwd(const ssa_problem* p, const void* q, const void* k, const void* v, void* o,
+                 const ssa_thresholds* th, uint64_t* skipped_bh, uint64_t* total_bh,
+                 uint8_t* tile_mask, ssa_stream_t stream);
+
+/* nq_max = nk_max = ceil(max_b S_b / block): the tile_mask's last two dims. */
+int ssa_tile_mask_dims(const ssa_problem* p, int64_t* nq_max, int64_t* nk_max);
+
+/* ---- calibration ------------------------------------------------------- */
+/* Calibration pass ([TRITON] "Triton kernels", the calibration kernel):
+ * computes full (dense) attention into `o` while counting, for n thresholds
+ * at once, the KV tiles that the forward would skip at each lambda_k: one
+ * per-work-group row of counts, no atomics. Decisions use exactly the
+ * forward's arithmetic, so counts[w][k] equals the number of tiles the
+ * forward skips in work-group w at lambda_k.
+ *
+ *  lambdas  host double [n], ascending, each in (0, 1]; n in [1, 64]
+ *           (e.g. 16 values log-spaced over [1e-6, 0.7], or the threshold
+ *           trial list of [PR1166] "Usage")
+ *  counts   device int32 [num_wg, n]: counts[w * n + k]
+ *  tiles    device int32 [num_wg]: KV tiles visited by work-group w
+ * Work-group w enumerates (b, h, i) sequence-major, then head, then Q-block:
+ * w = sum_{b' < b} H * nQ_b' + h * nQ_b + i with nQ_b = ceil(S_b / block).
+ * num_wg comes from ssa_calib_num_workgroups.
+ * Errors: SSA_ERR_INVALID_ARG, SSA_ERR_UNSUPPORTED, SSA_ERR_THRESHOLD_RANGE,
+ * SSA_ERR_HIP. */
+int ssa_attn_calibrate(const ssa_problem* p, const void* q, const void* k, const void* v,
+                       void* o, const double* lambdas, int32_t n, int32_t* counts,
+                       int32_t* tiles, ssa_stream_t stream);
+
+int ssa_calib_num_workgroups(const ssa_problem* p, int64_t* num_wg);
+
+/* Host-side reduction of a calibration pass into per-sequence tile sparsity
+ * ("tile skip ratios", [README] "Quick Start"): sparsity[b * n + k] =
+ * sum of counts over sequence b's work-groups / sum of their tiles.
+ * counts/tiles are HOST copies of the calibrate outputs. Sequences with no
+ * tiles get NaN. */
+int ssa_calibration_sparsity(const ssa_problem* p, const int32_t* counts, const int32_t* tiles,
+                             int32_t n, double* sparsity);
+
+/* Log-space fit of scale_factor = a * exp(b * sparsity) ([README]
+ * introduction; [TRITON] "Calibration": log-space fitting minimises relative
+ * error and records the observed sparsity range). Point i is (lambda[i],
+ * sparsity[i], seq_k[i]) with scale_factor_i = lambda[i] * seq_k[i]; ordinary
+ * least squares of ln(scale_factor) on sparsity over the points with
+ * 0 < sparsity < 1 and lambda > 0 (0 and 1 are plateaus with no slope
+ * information). s_min / s_max are the smallest / largest fitted sparsity.
+ * All pointers are host. Errors: SSA_ERR_INVALID_ARG, SSA_ERR_FIT_DEGENERATE. */
+typedef struct ssa_calib_result {
+  double a, log_a, b;  /* scale_factor = a * exp(b * s) = exp(log_a + b * s) */
+  double s_min, s_max; /* observed sparsity range of the fitted points       */
+  int32_t n_used;      /* points used                                        */
+} ssa_calib_result;
+
+int ssa_calibration_fit(const double* lambda, const double* sparsity, const double* seq_k,
+                        int32_t n, ssa_calib_result* out);
+
+/* ---- threshold resolution ---------------------------------------------- */
+/* Resolve the user/checkpoint threshold sources into lambda and log2(lambda)
+ * for a sequence of seq_k keys. Fields are read only when their flag is set
+ * in `set`; the first available source wins, in this order:
+ *   1. raw log2 threshold                 ([TRITON] "Method": raw first)
+ *   2. fixed lambda                       ([README] "Threshold Modes")
+ *   3. scale factor: lambda = sf / seq_k  ([TRTLLM] "Priority Order" 1)
+ *   4. target sparsity with a formula: sf = a * exp(b * target) (a given as a
+ *      or log_a), lambda = sf / seq_k    ([README] "Threshold Modes";
+ *      [TRTLLM] "Priority Order" 2-3)
+ *   5. static default lambda = 0.1       ([README] "Threshold Modes")
+ * A target without (a or log_a) and b is SSA_ERR_NO_FORMULA ([TRTLLM] "Use
+ * Cases" 1b; [DOCS] "User Configuration"). With SSA_SPEC_RANGE set, a target
+ * outside [s_min, s_max] still resolves but returns SSA_WARN_EXTRAPOLATED
+ * ([README] "Known Issues"). lambda outside [0, 1] or NaN is
+ * SSA_ERR_THRESHOLD_RANGE; seq_k < 1 with sources 3-4 is SSA_ERR_INVALID_ARG.
+ * lambda = 0 gives log2_lambda = -inf (dense). All pointers are host. */
+#define SSA_SPEC_RAW_LOG2     (1u << 0)
+#define SSA_SPEC_LAMBDA       (1u << 1)
+#define SSA_SPEC_SCALE_FACTOR (1u << 2)
+#define SSA_SPEC_TARGET       (1u << 3)
+#define SSA_SPEC_A            (1u << 4)
+#define SSA_SPEC_LOG_A        (1u << 5)
+#define SSA_SPEC_B            (1u << 6)
+#define SSA_SPEC_RANGE        (1u << 7)
+
+typedef struct ssa_threshold_spec {
+  uint32_t set; /* OR of SSA_SPEC_* flags */
+  double raw_log2, lambda, scale_factor, target_sparsity;
+  double a, log_a, b, s_min, s_max;
+} ssa_threshold_spec;
+
+int ssa_resolve_threshold(const ssa_threshold_spec* spec, int64_t seq_k, double* lambda,
+                          double* log2_lambda);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* ssa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSA_H_ */

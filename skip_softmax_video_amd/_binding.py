@@ -1,0 +1,261 @@
+"""ctypes binding of libssa.so (the C ABI in include/ssa.h).
+
+Argument marshalling only: every step of the attention path runs in the
+library's HIP kernels or its C host code. torch is used for device memory and
+streams (tensor pointers and torch's current HIP stream). There is no CPU
+fallback: if the library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libssa.so")
+
+# ---- status codes (include/ssa.h) -------------------------------------------
+SSA_OK = 0
+SSA_WARN_EXTRAPOLATED = 1
+SSA_ERR_INVALID_ARG = -1
+SSA_ERR_UNSUPPORTED = -2
+SSA_ERR_THRESHOLD_RANGE = -3
+SSA_ERR_NO_FORMULA = -4
+SSA_ERR_FIT_DEGENERATE = -5
+SSA_ERR_HIP = -6
+
+THRESH_LAMBDA = 0
+THRESH_LOG2 = 1
+THRESH_SCALE_FACTOR = 2
+_KINDS = {"lambda": THRESH_LAMBDA, "log2": THRESH_LOG2, "scale_factor": THRESH_SCALE_FACTOR}
+
+SPEC_RAW_LOG2 = 1 << 0
+SPEC_LAMBDA = 1 << 1
+SPEC_SCALE_FACTOR = 1 << 2
+SPEC_TARGET = 1 << 3
+SPEC_A = 1 << 4
+SPEC_LOG_A = 1 << 5
+SPEC_B = 1 << 6
+SPEC_RANGE = 1 << 7
+
+EXPORTED = (
+    "ssa_attn_fwd", "ssa_tile_mask_dims", "ssa_attn_calibrate", "ssa_calib_num_workgroups",
+    "ssa_calibration_sparsity", "ssa_calibration_fit", "ssa_resolve_threshold", "ssa_status_string",
+)
+
+
+class SSAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("block", ctypes.c_int32), ("cu_seqlens", ctypes.POINTER(ctypes.c_int32)),
+        ("stride_token", ctypes.c_int64), ("stride_head", ctypes.c_int64), ("sm_scale", ctypes.c_double),
+    ]
+
+
+class Thresholds(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("count", ctypes.c_int32), ("values", ctypes.POINTER(ctypes.c_double))]
+
+
+class CalibResult(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_double), ("log_a", ctypes.c_double), ("b", ctypes.c_double),
+                ("s_min", ctypes.c_double), ("s_max", ctypes.c_double), ("n_used", ctypes.c_int32)]
+
+
+class ThresholdSpec(ctypes.Structure):
+    _fields_ = [("set", ctypes.c_uint32), ("raw_log2", ctypes.c_double), ("lambda_", ctypes.c_double),
+                ("scale_factor", ctypes.c_double), ("target_sparsity", ctypes.c_double),
+                ("a", ctypes.c_double), ("log_a", ctypes.c_double), ("b", ctypes.c_double),
+                ("s_min", ctypes.c_double), ("s_max", ctypes.c_double)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libssa.so (built by skip_softmax_video_amd.build). Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m skip_softmax_video_amd.build`; "
+                           "there is no fallback implementation")
+    lib = ctypes.CDLL(path)
+    P, V = ctypes.POINTER, ctypes.c_void_p
+    i32, i64, dbl = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    sig = {
+        "ssa_attn_fwd": [P(Problem), V, V, V, V, P(Thresholds), V, V, V, V],
+        "ssa_tile_mask_dims": [P(Problem), P(i64), P(i64)],
+        "ssa_attn_calibrate": [P(Problem), V, V, V, V, P(dbl), i32, V, V, V],
+        "ssa_calib_num_workgroups": [P(Problem), P(i64)],
+        "ssa_calibration_sparsity": [P(Problem), P(i32), P(i32), i32, P(dbl)],
+        "ssa_calibration_fit": [P(dbl), P(dbl), P(dbl), i32, P(CalibResult)],
+        "ssa_resolve_threshold": [P(ThresholdSpec), i64, P(dbl), P(dbl)],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.ssa_status_string.argtypes = [ctypes.c_int]
+    lib.ssa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().ssa_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> int:
+    if status < 0:
+        raise SSAError(status, where)
+    return status
+
+
+# ---- problem marshalling -----------------------------------------------------
+def make_problem(q, cu_seqlens, block: int, sm_scale: float = 0.0) -> Tuple[Problem, np.ndarray]:
+    """ssa_problem for a [T, H, D] tensor; returns (struct, cu array kept alive)."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    T, H, D = q.shape
+    prob = Problem(batch=len(cu) - 1, num_heads=H, head_dim=D, block=block,
+                   cu_seqlens=cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                   stride_token=q.stride(0), stride_head=q.stride(1), sm_scale=float(sm_scale))
+    return prob, cu
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check_qkv(q, k, v, o):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3:
+            raise ValueError(f"{name} must be a 3-D bf16 device tensor [T, H, D]")
+        if t.shape != q.shape or t.stride() != q.stride():
+            raise ValueError(f"{name} must match q's shape and strides")
+
+
+def tile_mask_dims(prob: Problem) -> Tuple[int, int]:
+    nq, nk = ctypes.c_int64(), ctypes.c_int64()
+    _check(load_library().ssa_tile_mask_dims(ctypes.byref(prob), ctypes.byref(nq), ctypes.byref(nk)),
+           "ssa_tile_mask_dims")
+    return nq.value, nk.value
+
+
+def calib_num_workgroups(prob: Problem) -> int:
+    n = ctypes.c_int64()
+    _check(load_library().ssa_calib_num_workgroups(ctypes.byref(prob), ctypes.byref(n)),
+           "ssa_calib_num_workgroups")
+    return n.value
+
+
+# ---- entry points -------------------------------------------------------------
+def attn_fwd(q, k, v, cu_seqlens, threshold: Union[float, Sequence[float]], kind: str = "lambda",
+             block: int = 128, sm_scale: float = 0.0, out=None, skipped=None, total=None,
+             tile_mask=None, stream=None):
+    """ssa_attn_fwd on torch tensors; returns `out` (allocated when None).
+
+    threshold: one value for every head, or H values (per head); `kind` is
+    "lambda", "log2" (raw) or "scale_factor" (lambda = sf / S_b).
+    skipped/total: optional uint64 device tensors [B*H]; tile_mask: optional
+    uint8 device tensor [B, H, nq, nk].
+    """
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, k, v, out)
+    prob, cu = make_problem(q, cu_seqlens, block, sm_scale)
+    vals = np.ascontiguousarray(np.atleast_1d(np.asarray(threshold, dtype=np.float64)))
+    th = Thresholds(kind=_KINDS[kind], count=vals.size, values=vals.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    st = load_library().ssa_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(th),
+                                     _ptr(skipped), _ptr(total), _ptr(tile_mask), _stream(stream))
+    _check(st, "ssa_attn_fwd")
+    return out
+
+
+def attn_calibrate(q, k, v, cu_seqlens, lambdas: Sequence[float], block: int = 128, sm_scale: float = 0.0,
+                   out=None, counts=None, tiles=None, stream=None):
+    """ssa_attn_calibrate; returns (out, counts [num_wg, n] int32, tiles [num_wg] int32) on the device."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    _check_qkv(q, k, v, out)
+    prob, cu = make_problem(q, cu_seqlens, block, sm_scale)
+    lam = np.ascontiguousarray(np.asarray(lambdas, dtype=np.float64))
+    nwg = calib_num_workgroups(prob)
+    if counts is None:
+        counts = torch.empty((nwg, lam.size), dtype=torch.int32, device=q.device)
+    if tiles is None:
+        tiles = torch.empty((nwg,), dtype=torch.int32, device=q.device)
+    st = load_library().ssa_attn_calibrate(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                           lam.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), lam.size,
+                                           _ptr(counts), _ptr(tiles), _stream(stream))
+    _check(st, "ssa_attn_calibrate")
+    return out, counts, tiles
+
+
+def calibration_sparsity(cu_seqlens, num_heads: int, head_dim: int, block: int, counts: np.ndarray,
+                         tiles: np.ndarray) -> np.ndarray:
+    """ssa_calibration_sparsity on host copies; returns [B, n] tile sparsity."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    c = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+    t = np.ascontiguousarray(np.asarray(tiles, dtype=np.int32))
+    n = c.shape[1]
+    prob = Problem(batch=len(cu) - 1, num_heads=num_heads, head_dim=head_dim, block=block,
+                   cu_seqlens=cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                   stride_token=num_heads * head_dim, stride_head=head_dim, sm_scale=0.0)
+    out = np.empty((len(cu) - 1, n), dtype=np.float64)
+    P = ctypes.POINTER
+    _check(load_library().ssa_calibration_sparsity(
+        ctypes.byref(prob), c.ctypes.data_as(P(ctypes.c_int32)), t.ctypes.data_as(P(ctypes.c_int32)), n,
+        out.ctypes.data_as(P(ctypes.c_double))), "ssa_calibration_sparsity")
+    return out
+
+
+def calibration_fit(lambdas, sparsity, seq_k) -> CalibResult:
+    """ssa_calibration_fit: log-space fit of scale_factor = a * exp(b * s)."""
+    lam = np.ascontiguousarray(np.asarray(lambdas, dtype=np.float64))
+    sp = np.ascontiguousarray(np.asarray(sparsity, dtype=np.float64))
+    sk = np.ascontiguousarray(np.broadcast_to(np.asarray(seq_k, dtype=np.float64), lam.shape))
+    res = CalibResult()
+    P = ctypes.POINTER
+    _check(load_library().ssa_calibration_fit(lam.ctypes.data_as(P(ctypes.c_double)),
+                                              sp.ctypes.data_as(P(ctypes.c_double)),
+                                              sk.ctypes.data_as(P(ctypes.c_double)), lam.size, ctypes.byref(res)),
+           "ssa_calibration_fit")
+    return res
+
+
+def resolve_threshold(seq_k: int, raw_log2=None, lam=None, scale_factor=None, target_sparsity=None,
+                      a=None, log_a=None, b=None, s_min=None, s_max=None) -> Tuple[int, float, float]:
+    """ssa_resolve_threshold; returns (status, lambda, log2 lambda). Errors raise SSAError."""
+    spec = ThresholdSpec()
+    for flag, name, val in ((SPEC_RAW_LOG2, "raw_log2", raw_log2), (SPEC_LAMBDA, "lambda_", lam),
+                            (SPEC_SCALE_FACTOR, "scale_factor", scale_factor),
+                            (SPEC_TARGET, "target_sparsity", target_sparsity), (SPEC_A, "a", a),
+                            (SPEC_LOG_A, "log_a", log_a), (SPEC_B, "b", b)):
+        if val is not None:
+            spec.set |= flag
+            setattr(spec, name, float(val))
+    if s_min is not None and s_max is not None:
+        spec.set |= SPEC_RANGE
+        spec.s_min, spec.s_max = float(s_min), float(s_max)
+    out_l, out_t = ctypes.c_double(), ctypes.c_double()
+    st = load_library().ssa_resolve_threshold(ctypes.byref(spec), int(seq_k), ctypes.byref(out_l), ctypes.byref(out_t))
+    _check(st, "ssa_resolve_threshold")
+    return st, out_l.value, out_t.value

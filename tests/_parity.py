@@ -1,0 +1,125 @@
+"""Helpers for GPU-vs-oracle parity tests (not collected by pytest).
+
+The GPU side is reached only through the C-ABI binding; the oracle side only
+through `oracle/`; both consume the same `synth` bf16 inputs.
+"""
+from __future__ import annotations
+
+import math
+import sys
+from typing import Dict, Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+from oracle import skip_softmax as osk
+from synth import bf16_bits_to_f32
+
+# Tolerances: skip bits exact outside a +-1e-3 (log2 units) band around the
+# threshold; outputs within max-abs 2e-2 / mean-abs 2e-3 of the fp64 oracle
+# run on the same bf16-rounded inputs.
+MARGIN_BAND = 1e-3
+O_MAX_ABS = 2e-2
+O_MEAN_ABS = 2e-3
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(bits: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).cuda()
+
+
+def to_f64(bits: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def gpu_forward(xd: Dict, cu, threshold, kind: str, block: int, mask: bool = True):
+    """Run ssa_attn_fwd; return (o fp32 numpy [T,H,D], skipped [B,H], total [B,H], mask or None)."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    B = len(cu) - 1
+    T, H, D = xd["q"].shape
+    skipped = torch.zeros(B * H, dtype=torch.int64, device="cuda")
+    total = torch.zeros(B * H, dtype=torch.int64, device="cuda")
+    tm = None
+    if mask:
+        prob, _ = ssa.make_problem(xd["q"], cu, block)
+        nq, nk = ssa.tile_mask_dims(prob)
+        tm = torch.empty((B, H, nq, nk), dtype=torch.uint8, device="cuda")
+    o = ssa.attn_fwd(xd["q"], xd["k"], xd["v"], cu, threshold, kind=kind, block=block,
+                     skipped=skipped, total=total, tile_mask=tm)
+    torch.cuda.synchronize()
+    return (o.float().cpu().numpy(), skipped.cpu().numpy().reshape(B, H), total.cpu().numpy().reshape(B, H),
+            None if tm is None else tm.cpu().numpy())
+
+
+def t_matrix(cu, H: int, threshold, kind: str) -> np.ndarray:
+    """[B, H] log2 thresholds as the oracle reads them (fp64)."""
+    B = len(cu) - 1
+    vals = np.broadcast_to(np.atleast_1d(np.asarray(threshold, np.float64)), (H,))
+    t = np.empty((B, H))
+    for b in range(B):
+        S = int(cu[b + 1] - cu[b])
+        for h in range(H):
+            v = float(vals[h])
+            if kind == "lambda":
+                lam = v
+            elif kind == "scale_factor":
+                lam = 0.0 if S == 0 else v / S
+            else:
+                t[b, h] = v
+                continue
+            t[b, h] = -math.inf if lam == 0 else math.log2(lam)
+    return t
+
+
+def compare_masks(gpu_mask: np.ndarray, ref: Dict, t_bh: np.ndarray, qblocks: Iterable[Tuple[int, int, int]]):
+    """Skip bits must agree except where the oracle margin |d - t| <= MARGIN_BAND.
+
+    Returns the number of band tiles and of band mismatches (reported, allowed).
+    """
+    band = mism = 0
+    for (b, h, i) in qblocks:
+        g = gpu_mask[b, h, i]
+        r = ref["mask"][b, h, i]
+        valid = r != osk.TILE_NONE
+        assert np.all(g[~valid] == osk.TILE_NONE), f"tile mask written beyond the sequence at {(b, h, i)}"
+        with np.errstate(invalid="ignore"):
+            near = np.abs(ref["d"][b, h, i] - t_bh[b, h]) <= MARGIN_BAND
+        bad = (g != r) & valid
+        band += int(np.sum(near & valid))
+        mism += int(np.sum(bad & near))
+        hard = bad & ~near
+        assert not np.any(hard), (f"skip decision mismatch outside the margin band at (b,h,i)={(b, h, i)} "
+                                  f"tiles {np.nonzero(hard)[0][:8]} d={ref['d'][b, h, i][hard][:8]} t={t_bh[b, h]}")
+    return band, mism
+
+
+def compare_outputs(o_gpu: np.ndarray, o_ref: np.ndarray, rows: Optional[np.ndarray] = None):
+    """max-abs / mean-abs of the GPU output against the oracle over computed rows."""
+    sel = ~np.isnan(o_ref)
+    diff = np.abs(o_gpu[sel] - o_ref[sel])
+    assert diff.size > 0
+    mx, mean = float(diff.max()), float(diff.mean())
+    assert np.all(np.isfinite(o_gpu[sel])), "non-finite GPU output"
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS, f"output mismatch: max-abs {mx:.3e} mean-abs {mean:.3e}"
+    return mx, mean
+
+
+def sample_qblocks(cu, H: int, block: int, heads: Sequence[int], per_head: int, seed: int):
+    """Deterministic sample of Q-blocks: first, last (often partial) and random ones."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for b in range(len(cu) - 1):
+        nq = osk.n_tiles(int(cu[b + 1] - cu[b]), block)
+        if nq == 0:
+            continue
+        for h in heads:
+            picks = {0, nq - 1}
+            while len(picks) < min(per_head, nq):
+                picks.add(int(rng.integers(nq)))
+            out += [(b, h, i) for i in sorted(picks)]
+    return out

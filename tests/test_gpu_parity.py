@@ -1,0 +1,232 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Runs on an MI355X only (marker `gpu`). Inputs come from the seeded `synth`
+generator; the oracle runs on the same bf16-rounded values.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import calibration as oc
+from oracle import skip_softmax as osk
+from synth import CONFIGS, make_inputs
+from synth.video_tokens import VideoTokenConfig
+from tests._parity import (compare_masks, compare_outputs, gpu_forward, log, sample_qblocks, t_matrix,
+                           to_device, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+# Small multi-tile ragged batch: 3072 / 300 / 0 / 129 / 64 tokens.
+RAGGED = VideoTokenConfig("ragged", ((6, 16, 32), (3, 10, 10), (0, 1, 1), (1, 3, 43), (1, 8, 8)),
+                          num_heads=3, head_dim=128, sigma=0.5, block=128, seed=7)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    import torch
+    import skip_softmax_video_amd as ssa
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ssa.load_library()
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+
+def _inputs(cfg, heads=None):
+    x = make_inputs(cfg, heads=heads)
+    xd = {n: to_device(x[n]) for n in ("q", "k", "v")}
+    return x, xd, x["cu_seqlens"]
+
+
+def _f64(x):
+    return {n: to_f64(x[n]) for n in ("q", "k", "v")}
+
+
+def _full_parity(cfg, threshold, kind="lambda", block=None):
+    block = block or cfg.block
+    x, xd, cu = _inputs(cfg)
+    xf = _f64(x)
+    H = cfg.num_heads
+    log(f"[{cfg.name}] D={cfg.head_dim} block={block} threshold={threshold} kind={kind}")
+    o, sk, tot, mask = gpu_forward(xd, cu, threshold, kind, block)
+    t = t_matrix(cu, H, threshold, kind)
+    ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, block)
+    wgs = osk.workgroups(cu, H, block)
+    band, mism = compare_masks(mask, ref, t, wgs)
+    forced = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, block, forced_mask=mask)
+    mx, mean = compare_outputs(o, forced["o"])
+    np.testing.assert_array_equal(sk, (mask == osk.TILE_SKIPPED).sum(axis=(2, 3)))
+    np.testing.assert_array_equal(tot, ref["total"])
+    log(f"  skipped {sk.sum()}/{tot.sum()} band tiles {band} band mismatches {mism} "
+        f"max-abs {mx:.2e} mean-abs {mean:.2e}")
+    return sk, tot, mask, o
+
+
+@pytest.mark.parametrize("lam", [0.0, 1e-3, 1e-1])
+def test_tiny_parity(lam):
+    sk, tot, _, _ = _full_parity(CONFIGS["tiny"], lam)
+    if lam == 0.0:
+        assert sk.sum() == 0
+    else:
+        assert sk.sum() > 0
+
+
+@pytest.mark.parametrize("lam", [0.0, 1e-2, 1.0])
+def test_ragged_d128_parity(lam):
+    sk, tot, mask, _ = _full_parity(RAGGED, lam)
+    assert tot[2].sum() == 0 and np.all(mask[2] == osk.TILE_NONE)
+    if lam > 0:
+        assert sk.sum() > 0
+
+
+@pytest.mark.parametrize("head_dim,block", [(64, 128), (128, 64)])
+def test_other_tile_shapes(head_dim, block):
+    cfg = VideoTokenConfig("mixed", ((4, 13, 20), (1, 5, 9)), num_heads=2, head_dim=head_dim, sigma=0.5,
+                           block=block, seed=9)
+    sk, _, _, _ = _full_parity(cfg, 1e-1, block=block)
+    assert sk.sum() > 0
+
+
+def test_varlen_per_head_scale_factor():
+    # per-head scale factors; heads 0-1 dense (sf = 0), lambda_bh = sf_h / S_b
+    sf = [0.0, 0.0, 60.0]
+    sk, tot, mask, _ = _full_parity(RAGGED, sf, kind="scale_factor")
+    assert sk[:, :2].sum() == 0 and sk[:, 2].sum() > 0
+    # 300 / 64 keys is lambda > 1 on the shortest sequence: refused, nothing launched
+    import skip_softmax_video_amd as ssa
+    x, xd, cu = _inputs(RAGGED)
+    with pytest.raises(ssa.SSAError) as e:
+        ssa.attn_fwd(xd["q"], xd["k"], xd["v"], cu, [0.0, 0.0, 300.0], kind="scale_factor", block=128)
+    assert e.value.status == ssa.SSA_ERR_THRESHOLD_RANGE
+
+
+def test_calibration_counts_and_fit():
+    import torch
+    import skip_softmax_video_amd as ssa
+    cfg = RAGGED
+    x, xd, cu = _inputs(cfg)
+    xf = _f64(x)
+    lams = np.geomspace(1e-6, 0.7, 16)
+    o_cal, counts, tiles = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, lams, block=cfg.block)
+    torch.cuda.synchronize()
+    counts, tiles = counts.cpu().numpy(), tiles.cpu().numpy()
+    wgs = osk.workgroups(cu, cfg.num_heads, cfg.block)
+    # the calibration output is the dense output, bit for bit
+    o0, _, _, _ = gpu_forward(xd, cu, 0.0, "lambda", cfg.block, mask=False)
+    np.testing.assert_array_equal(o_cal.float().cpu().numpy(), o0)
+    # counts equal the forward's skipped tiles at each lambda_k, exactly
+    ts = np.log2(lams)
+    ref_d = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, -math.inf, cfg.block, fast=True)["d"]
+    cal_ref = osk.calibration_counts(xf["q"], xf["k"], xf["v"], cu, ts, cfg.block)
+    np.testing.assert_array_equal(tiles, cal_ref["tiles"])
+    total_band = 0
+    for kk, lam in enumerate(lams):
+        _, _, _, mask = gpu_forward(xd, cu, lam, "lambda", cfg.block)
+        per_wg = np.array([(mask[b, h, i] == osk.TILE_SKIPPED).sum() for (b, h, i) in wgs])
+        np.testing.assert_array_equal(counts[:, kk], per_wg)
+        band = np.array([np.sum(np.abs(ref_d[b, h, i] - ts[kk]) <= 1e-3) for (b, h, i) in wgs])
+        assert np.all(np.abs(counts[:, kk] - cal_ref["counts"][:, kk]) <= band)
+        total_band += band.sum()
+    log(f"  calibration counts ok; band tiles over 16 thresholds: {total_band}")
+    # per-sequence sparsity and the log-space fit through the C ABI
+    sp = ssa.calibration_sparsity(cu, cfg.num_heads, cfg.head_dim, cfg.block, counts, tiles)
+    nwg0 = cfg.num_heads * osk.n_tiles(int(cu[1] - cu[0]), cfg.block)  # the 3072-token sequence
+    fit = ssa.calibration_fit(lams, sp[0], float(cu[1] - cu[0]))
+    ref_sp = cal_ref["counts"][:nwg0].sum(0) / cal_ref["tiles"][:nwg0].sum()
+    ref_fit = oc.fit_exponential_logspace(lams, ref_sp, float(cu[1] - cu[0]))
+    assert fit.b == pytest.approx(ref_fit.b, rel=1e-3)
+    assert fit.a == pytest.approx(ref_fit.a, rel=1e-3)
+
+
+def test_determinism():
+    import torch
+    import skip_softmax_video_amd as ssa
+    x, xd, cu = _inputs(RAGGED)
+    r1 = gpu_forward(xd, cu, 1e-2, "lambda", 128)
+    r2 = gpu_forward(xd, cu, 1e-2, "lambda", 128)
+    for a, b in zip(r1, r2):
+        np.testing.assert_array_equal(a, b)
+    c1 = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, [1e-4, 1e-2], block=128)
+    c2 = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, [1e-4, 1e-2], block=128)
+    torch.cuda.synchronize()
+    for a, b in zip(c1, c2):
+        assert torch.equal(a, b)
+
+
+def test_untouched_memory_outside_valid_rows():
+    """Output rows of other heads / padding stay untouched (strided layout with a gap)."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    cfg = VideoTokenConfig("gap", ((1, 10, 20),), num_heads=2, head_dim=64, sigma=0.5, block=64, seed=3)
+    x = make_inputs(cfg)
+    T, H, D = x["q"].shape
+    big = {}
+    for n in ("q", "k", "v"):
+        buf = torch.zeros((T, H + 1, D), dtype=torch.bfloat16, device="cuda")  # head slot H is padding
+        buf[:, :H] = to_device(x[n])
+        big[n] = buf[:, :H]
+    out_buf = torch.full((T, H + 1, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    o = ssa.attn_fwd(big["q"], big["k"], big["v"], x["cu_seqlens"], 0.0, block=64, out=out_buf[:, :H])
+    torch.cuda.synchronize()
+    assert torch.all(out_buf[:, H] == 7.0)
+    ref = osk.skip_softmax_forward(*(to_f64(x[n]) for n in ("q", "k", "v")), x["cu_seqlens"], -math.inf, 64)
+    compare_outputs(o.float().cpu().numpy(), ref["o"])
+
+
+def _sampled_parity(cfg, lams, heads, per_head):
+    """Full-size launch; outputs and skip bits checked on sampled Q-blocks
+    (first, last/partial and random ones) that the oracle computes one by one."""
+    x, xd, cu = _inputs(cfg)
+    H, blk = cfg.num_heads, cfg.block
+    scale = osk.default_sm_scale(cfg.head_dim)
+    qbs = sample_qblocks(cu, H, blk, heads, per_head, seed=cfg.seed)
+    fracs = []
+    for lam in lams:
+        log(f"[{cfg.name}] lambda={lam}: GPU forward (full launch)")
+        o, sk, tot, mask = gpu_forward(xd, cu, lam, "lambda", blk)
+        t = t_matrix(cu, H, lam, "lambda")
+        want_tot = np.array([[osk.n_tiles(int(cu[b + 1] - cu[b]), blk) ** 2] * H for b in range(len(cu) - 1)])
+        np.testing.assert_array_equal(tot, want_tot)
+        np.testing.assert_array_equal(sk, (mask == osk.TILE_SKIPPED).sum(axis=(2, 3)))
+        log(f"  oracle on {len(qbs)} sampled Q-blocks")
+        band = mism = 0
+        worst_max, sum_abs, n_abs = 0.0, 0.0, 0
+        cache = {}
+        for (b, h, i) in qbs:
+            s0, s1 = int(cu[b]), int(cu[b + 1])
+            if (b, h) not in cache:
+                cache.clear()
+                cache[(b, h)] = (to_f64(x["k"][s0:s1, h]), to_f64(x["v"][s0:s1, h]))
+            kh, vh = cache[(b, h)]
+            r0, r1 = i * blk, min(s1 - s0, (i + 1) * blk)
+            qh = to_f64(x["q"][s0 + r0:s0 + r1, h])
+            nk = osk.n_tiles(s1 - s0, blk)
+            d, _ = osk.tile_stats_fast(qh, kh, blk, scale)
+            ref_skip = d < t[b, h]
+            gpu_skip = mask[b, h, i, :nk] == osk.TILE_SKIPPED
+            assert np.all(mask[b, h, i, nk:] == osk.TILE_NONE)
+            near = np.abs(d - t[b, h]) <= 1e-3
+            hard = (gpu_skip != ref_skip) & ~near
+            assert not np.any(hard), f"skip mismatch at {(b, h, i)} tiles {np.nonzero(hard)[0][:8]}"
+            band += int(near.sum())
+            mism += int(((gpu_skip != ref_skip) & near).sum())
+            ref = osk.skip_softmax_qblock(qh, kh, vh, t[b, h], blk, scale, forced_skip=gpu_skip)
+            diff = np.abs(o[s0 + r0:s0 + r1, h] - ref["o"])
+            worst_max = max(worst_max, float(diff.max()))
+            sum_abs += float(diff.sum())
+            n_abs += diff.size
+        mean = sum_abs / n_abs
+        assert worst_max <= 2e-2 and mean <= 2e-3, f"output mismatch max {worst_max:.3e} mean {mean:.3e}"
+        frac = sk.sum() / tot.sum()
+        log(f"  sparsity {frac:.4f} band {band} band-mismatch {mism} max-abs {worst_max:.2e} mean-abs {mean:.2e}")
+        fracs.append(frac)
+    return fracs
+
+
+def test_wan5b_sampled_parity():
+    fr = _sampled_parity(CONFIGS["wan5b"], [0.0, 1e-3], heads=[0, 11, 23], per_head=3)
+    assert fr[0] == 0.0 and fr[1] > 0.0
+
+
+def test_headline_sampled_parity():
+    fr = _sampled_parity(CONFIGS["headline"], [0.0, 8e-3], heads=[0, 19, 39], per_head=3)
+    assert fr[0] == 0.0 and fr[1] > 0.3

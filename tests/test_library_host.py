@@ -1,0 +1,183 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+its host-side logic (threshold resolution, fit, calibration reduction,
+argument validation) matches the oracle. No GPU call is made here: every
+forward/calibrate call below fails validation before any HIP work."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import skip_softmax_video_amd as ssa
+from skip_softmax_video_amd import _binding as bnd
+from oracle import calibration as oc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ssa.load_library()
+    decl = set()
+    for name in os.listdir(os.path.join(ROOT, "include")):
+        if name.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", name)).read()
+            decl |= set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s+(ssa_\w+)\s*\(", text, re.M))
+    assert decl, "no declarations found"
+    assert decl == set(ssa.EXPORTED)
+    for sym in decl:
+        assert hasattr(lib, sym), sym
+
+
+RESOLVE_CASES = [
+    dict(raw_log2=-0.7), dict(lam=0.61557), dict(), dict(scale_factor=5000.0),
+    dict(target_sparsity=0.5, a=7.93, b=8.61), dict(target_sparsity=0.7, log_a=math.log(7.93), b=8.61),
+    dict(target_sparsity=0.25, a=7.93, b=8.61, s_min=0.38, s_max=0.86),
+    dict(raw_log2=-1.0, lam=0.25, scale_factor=100.0), dict(lam=0.0), dict(raw_log2=-math.inf),
+]
+
+
+@pytest.mark.parametrize("case", RESOLVE_CASES)
+@pytest.mark.parametrize("seq_k", [8190, 32760, 75600])
+def test_resolve_matches_oracle(case, seq_k):
+    okw = dict(case)
+    if "lam" in okw:
+        okw["lam"] = okw.pop("lam")
+    want = oc.resolve_threshold(oc.ThresholdSpec(**okw), seq_k)
+    got = ssa.resolve_threshold(seq_k, **case)
+    assert got[0] == want[0]
+    assert got[1] == pytest.approx(want[1], rel=1e-15, abs=0)
+    assert got[2] == pytest.approx(want[2], rel=1e-15, abs=0) or (math.isinf(got[2]) and got[2] == want[2])
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(target_sparsity=0.5), ssa.SSA_ERR_NO_FORMULA),
+    (dict(target_sparsity=0.5, b=1.0), ssa.SSA_ERR_NO_FORMULA),
+    (dict(lam=1.5), ssa.SSA_ERR_THRESHOLD_RANGE),
+    (dict(lam=-0.1), ssa.SSA_ERR_THRESHOLD_RANGE),
+    (dict(lam=float("nan")), ssa.SSA_ERR_THRESHOLD_RANGE),
+    (dict(raw_log2=0.5), ssa.SSA_ERR_THRESHOLD_RANGE),
+    (dict(scale_factor=5000.0), ssa.SSA_ERR_THRESHOLD_RANGE),   # over 1024 keys: lambda 4.88
+])
+def test_resolve_errors(case, status):
+    with pytest.raises(ssa.SSAError) as e:
+        ssa.resolve_threshold(1024, **case)
+    assert e.value.status == status
+    want = oc.resolve_threshold(oc.ThresholdSpec(**case), 1024)[0]
+    assert want == status
+
+
+def test_fit_matches_oracle_and_degenerate():
+    rng = np.random.default_rng(2)
+    for trial in range(20):
+        n = int(rng.integers(2, 17))
+        s = np.concatenate([rng.uniform(0, 1, n), [0.0, 1.0]])
+        lam = np.geomspace(1e-6, 0.7, s.size)
+        sk = rng.choice([8190.0, 32760.0, 75600.0], size=s.size)
+        try:
+            want = oc.fit_exponential_logspace(lam, s, sk)
+        except ValueError:
+            with pytest.raises(ssa.SSAError):
+                ssa.calibration_fit(lam, s, sk)
+            continue
+        got = ssa.calibration_fit(lam, s, sk)
+        assert got.b == pytest.approx(want.b, rel=1e-10)
+        assert got.log_a == pytest.approx(want.log_a, rel=1e-10, abs=1e-12)
+        assert (got.s_min, got.s_max, got.n_used) == (want.s_min, want.s_max, want.n_used)
+    with pytest.raises(ssa.SSAError) as e:
+        ssa.calibration_fit([1e-3, 1e-2], [0.5, 0.5], 100.0)
+    assert e.value.status == ssa.SSA_ERR_FIT_DEGENERATE
+
+
+def test_calibration_sparsity_reduction():
+    cu = [0, 1000, 1000, 129]
+    cu = np.cumsum([0, 1000, 0, 129])
+    H, blk, n = 3, 128, 4
+    nwg = (8 + 0 + 2) * H
+    rng = np.random.default_rng(0)
+    tiles = np.array([8] * 24 + [2] * 6, dtype=np.int32)
+    counts = np.sort(rng.integers(0, 3, size=(nwg, n)), axis=1).astype(np.int32)
+    sp = ssa.calibration_sparsity(cu, H, 128, blk, counts, tiles)
+    assert sp.shape == (3, n)
+    np.testing.assert_allclose(sp[0], counts[:24].sum(0) / tiles[:24].sum())
+    assert np.all(np.isnan(sp[1]))
+    np.testing.assert_allclose(sp[2], counts[24:].sum(0) / tiles[24:].sum())
+
+
+def _problem(**kw):
+    cu = np.asarray(kw.pop("cu", [0, 256]), dtype=np.int32)
+    base = dict(batch=len(cu) - 1, num_heads=2, head_dim=128, block=128,
+                cu_seqlens=cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                stride_token=256, stride_head=128, sm_scale=0.0)
+    base.update(kw)
+    return bnd.Problem(**base), cu
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("kw,th,status", [
+    (dict(head_dim=96), (0, [0.1]), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(block=32), (0, [0.1]), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(num_heads=0), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(num_heads=600, stride_token=600 * 128), (0, [0.1]), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(cu=[0, 10, 5]), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(cu=[3, 10]), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(stride_token=100), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(sm_scale=-1.0), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(), (0, [1.5]), ssa.SSA_ERR_THRESHOLD_RANGE),
+    (dict(), (0, [float("nan")]), ssa.SSA_ERR_THRESHOLD_RANGE),
+    (dict(), (1, [0.25]), ssa.SSA_ERR_THRESHOLD_RANGE),            # raw log2 > 0
+    (dict(), (2, [300.0]), ssa.SSA_ERR_THRESHOLD_RANGE),           # sf / 256 > 1
+    (dict(), (0, [0.1, 0.1, 0.1]), ssa.SSA_ERR_INVALID_ARG),       # count not 1 or H
+    (dict(), (7, [0.1]), ssa.SSA_ERR_INVALID_ARG),                 # unknown kind
+])
+def test_forward_argument_errors(kw, th, status):
+    lib = ssa.load_library()
+    prob, cu = _problem(**kw)
+    vals = np.asarray(th[1], dtype=np.float64)
+    t = bnd.Thresholds(kind=th[0], count=vals.size, values=vals.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    st = lib.ssa_attn_fwd(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, ctypes.byref(t), None, None, None, None)
+    assert st == status, ssa.status_string(st)
+
+
+def test_forward_null_and_misaligned_pointers():
+    lib = ssa.load_library()
+    prob, cu = _problem()
+    vals = np.asarray([0.1])
+    t = bnd.Thresholds(kind=0, count=1, values=vals.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    assert lib.ssa_attn_fwd(ctypes.byref(prob), None, FAKE, FAKE, FAKE, ctypes.byref(t), None, None, None, None) \
+        == ssa.SSA_ERR_INVALID_ARG
+    assert lib.ssa_attn_fwd(ctypes.byref(prob), FAKE + 8, FAKE, FAKE, FAKE, ctypes.byref(t), None, None, None,
+                            None) == ssa.SSA_ERR_INVALID_ARG
+    assert lib.ssa_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, ctypes.byref(t), None, None, None, None) \
+        == ssa.SSA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("lams,status", [
+    ([0.0, 0.1], ssa.SSA_ERR_THRESHOLD_RANGE),
+    ([0.1, 1.5], ssa.SSA_ERR_THRESHOLD_RANGE),
+    ([0.1, 0.01], ssa.SSA_ERR_INVALID_ARG),     # not ascending
+    ([0.1] * 65, ssa.SSA_ERR_INVALID_ARG),      # more than 64 thresholds
+    ([], ssa.SSA_ERR_INVALID_ARG),
+])
+def test_calibrate_argument_errors(lams, status):
+    lib = ssa.load_library()
+    prob, cu = _problem()
+    lam = np.asarray(lams, dtype=np.float64)
+    st = lib.ssa_attn_calibrate(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE,
+                                lam.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), lam.size, FAKE, FAKE, None)
+    assert st == status
+
+
+def test_workgroup_and_mask_dims():
+    prob, cu = _problem(cu=np.cumsum([0, 75600, 32760, 8190]).tolist(), num_heads=40, stride_token=40 * 128)
+    assert ssa.calib_num_workgroups(prob) == 40 * (591 + 256 + 64)
+    assert ssa.tile_mask_dims(prob) == (591, 591)
+
+
+def test_status_strings():
+    for code in (0, 1, -1, -2, -3, -4, -5, -6):
+        assert ssa.status_string(code) and ssa.status_string(code) != "unknown status"
+    assert ssa.status_string(99) == "unknown status"
