@@ -33,6 +33,9 @@ int validate_problem(const ssa_problem* p) {
     if (s < 0) return SSA_ERR_INVALID_ARG;
     // work-groups of one sequence and tile-mask rows are indexed in int32
     if (ceil_div(s, p->block) * p->num_heads > INT32_MAX / 2) return SSA_ERR_UNSUPPORTED;
+    // K/V tiles are fetched through 32-bit buffer offsets from the head's first row
+    if (s > 0 && ((s - 1) * p->stride_token + p->block * p->stride_token + p->head_dim) * 2 > (int64_t)UINT32_MAX)
+      return SSA_ERR_UNSUPPORTED;
   }
   // 16-byte aligned rows; distinct tokens (and heads, when H > 1) start at
   // least one row apart. Full non-overlap of the layout is the caller's duty.

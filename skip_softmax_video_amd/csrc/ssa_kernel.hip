@@ -12,27 +12,38 @@
 //
 // Work decomposition (one work-group = one Br-row Q-block of one head):
 //   * Br = Bc = BLK query rows / keys per tile; BLK/32 waves, each owning 32
-//     query rows. D = head dim.
+//     query rows. D = head dim. Two work-groups share a CU (<= 256 VGPRs +
+//     AGPRs per wave, 64 KB of LDS per work-group), so one work-group's
+//     softmax VALU work overlaps the other's MFMA work.
 //   * Scores are computed transposed, S^T = K_j Q^T, with
 //     v_mfma_f32_32x32x16_bf16: lane l then holds query (l % 32) and 16 keys
 //     per 32-key block, so the per-row max and sum are in-register
-//     reductions plus one exchange with lane l ^ 32.
+//     reductions plus one v_permlane32_swap with lane l ^ 32.
 //   * The same registers, rounded to bf16, are the B operand of
-//     O^T += V_j^T P^T; V_j^T comes straight from the row-major V tile in LDS
-//     through ds_read_b64_tr_b16 (4x16 transposing LDS read), so V needs no
-//     register transpose. The per-lane key order inside a 16-key MFMA step is
-//     permuted identically on both operands (the contraction does not care).
+//     O^T += V_j^T P^T; V_j^T is read from the row-major V tile in LDS with
+//     ds_read_b64_tr_b16 (4x16 transposing read). The per-lane key order
+//     inside a 16-key MFMA step is permuted identically on both operands.
 //   * O^T accumulates in registers; lane l owns query (l % 32), so the
-//     online-softmax rescale factor and row sum are per-lane scalars.
+//     rescale factor and row sum are per-lane scalars. The accumulator is
+//     rescaled lazily: the exponent base only moves when some row's maximum
+//     rose by more than 2^8, which keeps P <= 256 and the result unchanged
+//     up to rounding.
+//   * K and V tiles go global -> LDS with global_load_lds_dwordx4 (no
+//     register staging). Each wave instruction fills 1 KB of LDS; the
+//     16-byte granules of a row are XOR-swizzled so that the MFMA operand
+//     reads (ds_read_b128 for K, ds_read_b64_tr_b16 for V) avoid bank
+//     conflicts. Rows past the end of a sequence re-read the last valid row
+//     (finite values): their scores are masked to -inf and their P is 0.
 //   * Skip vote: every lane forms x = rowmax * sm_scale * log2(e) - m for its
-//     query (m = running max before the tile, -inf on the first tile, so x =
-//     +inf and the first tile is always kept); the wave max goes to LDS and
-//     the work-group max d decides for the whole tile: skip iff d < t.
-//     The calibration instantiation evaluates d < t_k for up to 64
-//     thresholds, one per lane of wave 0, never skips, and writes one row of
-//     counts per work-group (no atomics).
-//   * K_{j+1} is prefetched into registers before the vote; V_j is read
-//     from global memory only after the vote kept the tile.
+//     query (m = running max before the tile; -inf on the first tile, so x =
+//     +inf and the first tile is always kept). A wave keeps the tile if any
+//     valid lane has x >= t (one ballot); the work-group ORs the waves'
+//     flags through LDS, so d = max_r x_r < t exactly when nobody keeps.
+//     The calibration instantiation takes one ballot per threshold, never
+//     skips, and writes one row of counts per work-group (no atomics).
+//   * V_j is fetched only when the vote kept the tile, issued right after
+//     the vote so that it lands while the softmax runs; K_{j+1} is fetched
+//     as soon as every wave is done reading K_j.
 //   * Work-groups are remapped so that each XCD (8 per MI355X, 4 MB L2 each)
 //     receives a contiguous range of Q-blocks of the same head: co-resident
 //     work-groups stream the same K/V tiles through their XCD's L2.
@@ -52,6 +63,12 @@ typedef float floatx8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Exponent-base slack of the lazy rescale (log2 units): P <= 2^8.
+constexpr float kRescaleSlack = 8.0f;
+// Buffer descriptor word 3 for raw (untyped) dword access on gfx9-family parts.
+constexpr int kBufferFlags = 0x00020000;
 
 template <int D, int BLK>
 struct Shape {
@@ -61,59 +78,97 @@ struct Shape {
   static constexpr int DS = D / 16;       // 16-wide d steps of S^T = K Q^T
   static constexpr int MB = D / 32;       // 32-wide d blocks of O^T
   static constexpr int KS = BLK / 16;     // 16-key steps of O^T += V^T P^T
-  static constexpr int K_LD = D + 8;      // K row stride in LDS (elements): +16 B
-  static constexpr int V_LD = D + 16;     // V row stride in LDS (elements): +32 B
-  static constexpr int CH = D / 8;        // 16-byte chunks per row
-  static constexpr int LOADS = BLK * CH / NT;  // 16-byte loads per thread per tile
-  static_assert(BLK * CH % NT == 0, "tile must split evenly over the threads");
+  static constexpr int CH = D / 8;        // 16-byte granules per row
+  static constexpr int GRAN = BLK * CH;   // granules per tile
+  static constexpr int DMA = GRAN / NT;   // direct loads per thread per tile
+  static_assert(GRAN % NT == 0, "tile must split evenly over the threads");
+  static_assert(CH == 8 || CH == 16, "head_dim 64 or 128");
 };
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
+// XOR swizzle of the 16-byte granules of a K row: the 32 rows read by one
+// ds_read_b128 (same granule column) land on distinct bank groups.
+template <int CH>
+__device__ __forceinline__ int swz_k(int row) { return row & (CH - 1); }
+
+// XOR swizzle of a V row: one ds_read_b64_tr_b16 reads 4 consecutive rows x
+// 2 granules per 16 lanes (4 granules per 32 lanes); these land on distinct
+// bank groups for 32- and 64-bank LDS alike.
+template <int CH>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (CH == 16) {
+    return (0xCA60 >> (4 * (row & 3))) & 15;  // rows 0..3 -> 0, 6, 10, 12
+  } else {
+    return 2 * (row & 3);
+  }
 }
+
+// global -> LDS copy of one BLK x D tile with buffer_load_dwordx4 ... lds.
+// The buffer descriptor covers exactly the head's valid rows (base = the
+// head's first row, `bytes` = extent of rows [0, S)), so rows past the end of
+// the sequence read as zero (hardware range check, no branch).
+// Wave w's instruction i fills granules [g0, g0 + 64) of the LDS tile, g0 =
+// (i * NW + w) * 64; lane l fills granule g0 + l, i.e. row (g0 + l) / CH at
+// swizzled position (g0 + l) % CH, and so loads logical granule
+// position ^ swz(row) of that row. An instruction covers RPI = 64 / CH rows;
+// the row offset goes in the scalar soffset, the lane's position within the
+// instruction in a per-lane voffset that does not change between tiles.
+template <int D>
+__device__ __forceinline__ uint32_t head_extent(int rows, int64_t stride_tok) {
+  return rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * stride_tok + D) * 2) : 0u;
+}
+
+template <int D, int BLK, bool IS_V>
+__device__ __forceinline__ void dma_load(const uint16_t* head, uint32_t bytes, uint16_t* lds, int row0,
+                                         int64_t stride_tok, int wave, int lane) {
+  using SH = Shape<D, BLK>;
+  constexpr int RPI = 64 / SH::CH;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)head, 0, bytes, kBufferFlags);
+  const int lrow = lane / SH::CH;
+#pragma unroll
+  for (int i = 0; i < SH::DMA; ++i) {
+    const int rin = RPI * (i * SH::NW + wave);  // first row of this instruction within the tile
+    const int row = rin + lrow;
+    const int chunk = (lane % SH::CH) ^ (IS_V ? swz_v<SH::CH>(row) : swz_k<SH::CH>(row));
+    const uint32_t voff = (uint32_t)(((int64_t)lrow * stride_tok + chunk * 8) * 2);
+    const uint32_t soff = (uint32_t)((int64_t)(row0 + rin) * stride_tok * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + (i * SH::NW + wave) * 512), 16, voff, soff, 0,
+                                             0);
+  }
+}
+
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Load one BLK x D bf16 tile (rows row0.. of the head, row-major, 16 B per
-// thread per step, 16 consecutive threads per 256-byte row) into registers;
-// rows at or beyond `nvalid` read as zero.
-template <int D, int BLK>
-__device__ __forceinline__ void load_tile(uint4* r, const uint16_t* base,
-                                          int64_t stride_tok, int nvalid, int tid) {
-  using SH = Shape<D, BLK>;
-#pragma unroll
-  for (int i = 0; i < SH::LOADS; ++i) {
-    const int c = i * SH::NT + tid;
-    const int row = c / SH::CH;
-    const int col = (c % SH::CH) * 8;
-    r[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (row < nvalid) r[i] = *reinterpret_cast<const uint4*>(base + (int64_t)row * stride_tok + col);
-  }
+// max / sum of a value and its partner in lane l ^ 32
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int BLK, int LD>
-__device__ __forceinline__ void store_tile(uint16_t* lds, const uint4* r, int tid) {
-  using SH = Shape<D, BLK>;
-#pragma unroll
-  for (int i = 0; i < SH::LOADS; ++i) {
-    const int c = i * SH::NT + tid;
-    const int row = c / SH::CH;
-    const int col = (c % SH::CH) * 8;
-    *reinterpret_cast<uint4*>(lds + row * LD + col) = r[i];
-  }
+// A operand of S^T = K Q^T for key block kb, d step s: K[32 kb + l32][16 s + 8 hl .. + 7]
+template <class SH>
+__device__ __forceinline__ bf16x8 read_k(const uint16_t* k_lds, int kb, int s, int l32, int hl) {
+  const int row = 32 * kb + l32;
+  const int gran = row * SH::CH + ((2 * s + hl) ^ swz_k<SH::CH>(row));
+  return *reinterpret_cast<const bf16x8*>(k_lds + gran * 8);
 }
+
+__device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
 template <int D, int BLK, bool CALIB>
-__global__ __launch_bounds__(2 * BLK) void fwd_kernel(const LaunchParams p) {  // 2*BLK = Shape::NT
+__global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {  // 2*BLK = Shape::NT
   using SH = Shape<D, BLK>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BLK * SH::K_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[BLK * SH::V_LD];
-  __shared__ float red[SH::NW];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[BLK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[BLK * D];
+  __shared__ uint64_t vote[SH::NW];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps tile addressing scalar
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
@@ -136,6 +191,11 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(const LaunchParams p) {  /
   const int nK = nQ;
   const int H = p.num_heads;
   const int64_t head_off = (int64_t)tok0 * p.stride_tok + (int64_t)h * p.stride_head;
+  const uint16_t* kbase = p.k + head_off;
+  const uint16_t* vbase = p.v + head_off;
+
+  const uint32_t head_bytes = head_extent<D>(S, p.stride_tok);
+  dma_load<D, BLK, false>(kbase, head_bytes, k_lds, 0, p.stride_tok, wave, lane);
 
   // ---- Q fragment: B operand of S^T = K Q^T, held for the whole loop ------
   const int qrow = qb * BLK + wave * 32 + l32;
@@ -153,39 +213,46 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(const LaunchParams p) {  /
 
   const float c2 = p.scale_log2;
   const float t = CALIB ? 0.0f : p.t_bh[b * H + h];
-  float tcal = -INFINITY;
+  const int ncal = CALIB ? p.ncal : 0;
   int ncount = 0;
-  if (CALIB && lane < p.ncal) tcal = p.cal_t[lane];
 
-  float m = -INFINITY;   // running max, log2 units
-  float l = 0.0f;        // partial row sum over this lane's keys
+  float m_true = -INFINITY;  // running max of the method (log2 units), updated on kept tiles
+  float m_use = -INFINITY;   // exponent base, m_use <= m_true < m_use + slack
+  float l = 0.0f;            // partial row sum over this lane's keys
   floatx16 acc[SH::MB];
 #pragma unroll
   for (int mb = 0; mb < SH::MB; ++mb) acc[mb] = floatx16{};
   int skipped = 0;
 
-  const uint16_t* kbase = p.k + head_off;
-  const uint16_t* vbase = p.v + head_off;
-  uint4 regs[SH::LOADS];
-  load_tile<D, BLK>(regs, kbase, p.stride_tok, min(BLK, S), tid);
-  store_tile<D, BLK, SH::K_LD>(k_lds, regs, tid);
+  // V^T operand read positions (ds_read_b64_tr_b16): row within a 16-key
+  // step and byte offset within the row, before the swizzle.
+  const int tr_row = 4 * hl + ((lane & 15) >> 2);
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_elem = 4 * (lane & 1);  // element offset inside the granule
+
+  wait_dma();
   __syncthreads();
 
   for (int j = 0; j < nK; ++j) {
     const int nvalid = min(BLK, S - j * BLK);
 
     // ---- S^T = K_j Q^T (always paid) -------------------------------------
+    // operands of step s + 1 are read from LDS while step s multiplies
     floatx16 sc[SH::KB];
 #pragma unroll
     for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
+    bf16x8 ka[2][SH::KB];
+#pragma unroll
+    for (int kb = 0; kb < SH::KB; ++kb) ka[0][kb] = read_k<SH>(k_lds, kb, 0, l32, hl);
 #pragma unroll
     for (int s = 0; s < SH::DS; ++s) {
+      if (s + 1 < SH::DS) {
 #pragma unroll
-      for (int kb = 0; kb < SH::KB; ++kb) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(k_lds + (32 * kb + l32) * SH::K_LD + 16 * s + 8 * hl);
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc[kb], 0, 0, 0);
+        for (int kb = 0; kb < SH::KB; ++kb) ka[(s + 1) & 1][kb] = read_k<SH>(k_lds, kb, s + 1, l32, hl);
       }
+#pragma unroll
+      for (int kb = 0; kb < SH::KB; ++kb)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s & 1][kb], qf[s], sc[kb], 0, 0, 0);
     }
     if (nvalid < BLK) {
 #pragma unroll
@@ -203,82 +270,85 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(const LaunchParams p) {  /
     for (int kb = 0; kb < SH::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float rowmax = mx * c2;
-    const float x = qvalid ? rowmax - m : -INFINITY;  // m = -inf gives +inf
-    const float wx = wave_max(x);
-    if (lane == 0) red[wave] = wx;
-
-    // prefetch K_{j+1} while the vote settles
-    const bool more = j + 1 < nK;
-    if (more) load_tile<D, BLK>(regs, kbase + (int64_t)(j + 1) * BLK * p.stride_tok, p.stride_tok,
-                                min(BLK, S - (j + 1) * BLK), tid);
+    const float rowmax = xhalf_max(mx) * c2;
+    const float x = qvalid ? rowmax - m_true : -INFINITY;  // m_true = -inf gives +inf
+    if constexpr (CALIB) {
+      uint64_t bits = 0;  // bit k: some row of this wave keeps the tile at threshold k
+      for (int k = 0; k < ncal; ++k)
+        if (wave_any(x >= p.cal_t[k])) bits |= 1ull << k;
+      if (lane == 0) vote[wave] = bits;
+    } else {
+      const bool kw = wave_any(x >= t);
+      if (lane == 0) vote[wave] = kw ? 1ull : 0ull;
+    }
     __syncthreads();  // votes visible; every wave is done reading K_j and V_{j-1}
 
-    float d = red[0];
+    uint64_t all = vote[0];
 #pragma unroll
-    for (int w = 1; w < SH::NW; ++w) d = fmaxf(d, red[w]);
+    for (int w = 1; w < SH::NW; ++w) all |= vote[w];
     bool keep;
     if constexpr (CALIB) {
-      ncount += (d < tcal) ? 1 : 0;
+      if (lane < ncal) ncount += ((all >> lane) & 1ull) ? 0 : 1;
       keep = true;
     } else {
-      keep = !(d < t);
+      keep = all != 0;
       skipped += keep ? 0 : 1;
       if (p.tile_mask != nullptr && tid == 0)
         p.tile_mask[((int64_t)((p.seq_abs0 + b) * H + h) * p.mask_nq + qb) * p.mask_nk + j] = keep ? 0 : 1;
     }
 
-    if (more) store_tile<D, BLK, SH::K_LD>(k_lds, regs, tid);
+    if (j + 1 < nK) dma_load<D, BLK, false>(kbase, head_bytes, k_lds, (j + 1) * BLK, p.stride_tok, wave, lane);
+    bf16x8 pb[SH::KS];
     if (keep) {
-      uint4 vr[SH::LOADS];
-      load_tile<D, BLK>(vr, vbase + (int64_t)j * BLK * p.stride_tok, p.stride_tok, nvalid, tid);
-      store_tile<D, BLK, SH::V_LD>(v_lds, vr, tid);
+      dma_load<D, BLK, true>(vbase, head_bytes, v_lds, j * BLK, p.stride_tok, wave, lane);
+
+      // ---- online softmax (log2 domain), overlapping the V fetch ---------
+      m_true = fmaxf(m_true, rowmax);
+      if (wave_any(rowmax > m_use + kRescaleSlack)) {
+        const float m_new = fmaxf(m_use, rowmax);
+        const float alpha = fast_exp2(m_use - m_new);  // 0 when m_use was -inf
+        l *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < SH::MB; ++mb) acc[mb] *= alpha;
+        m_use = m_new;
+      }
+      const float nm = -m_use;
+#pragma unroll
+      for (int s = 0; s < SH::KS; ++s) {
+        floatx8 e;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          e[r] = fast_exp2(fmaf(sc[s >> 1][8 * (s & 1) + r], c2, nm));
+          l += e[r];
+        }
+        pb[s] = __builtin_convertvector(e, bf16x8);
+      }
     }
+    wait_dma();
     __syncthreads();  // K_{j+1} and V_j visible
 
     if (keep) {
-      // ---- online softmax (log2 domain) ----------------------------------
-      const float m_new = fmaxf(m, rowmax);
-      const float alpha = fast_exp2(m - m_new);  // 0 when m was -inf
-      const float nm = -m_new;
-      float ps = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < SH::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(sc[kb][r], c2, nm));
-          sc[kb][r] = e;
-          ps += e;
-        }
-      l = l * alpha + ps;
-      m = m_new;
-#pragma unroll
-      for (int mb = 0; mb < SH::MB; ++mb) acc[mb] *= alpha;
-
       // ---- O^T += V_j^T P^T ----------------------------------------------
-      const int tr_row = 4 * hl + ((lane & 15) >> 2);
-      const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
       for (int s = 0; s < SH::KS; ++s) {
-        const floatx8 pf = (s & 1) ? __builtin_shufflevector(sc[s >> 1], sc[s >> 1], 8, 9, 10, 11, 12, 13, 14, 15)
-                                   : __builtin_shufflevector(sc[s >> 1], sc[s >> 1], 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 pb = __builtin_convertvector(pf, bf16x8);
+        const int r_lo = 16 * s + tr_row;
+        const int r_hi = r_lo + 8;
 #pragma unroll
         for (int mb = 0; mb < SH::MB; ++mb) {
-          const uint16_t* vp = v_lds + (16 * s + tr_row) * SH::V_LD + 32 * mb + tr_col;
-          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp));
-          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(vp + 8 * SH::V_LD));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[mb], 0, 0, 0);
+          const int c = 4 * mb + tr_chunk;
+          const uint16_t* lo = v_lds + (r_lo * SH::CH + (c ^ swz_v<SH::CH>(r_lo))) * 8 + tr_elem;
+          const uint16_t* hi = v_lds + (r_hi * SH::CH + (c ^ swz_v<SH::CH>(r_hi))) * 8 + tr_elem;
+          const shortx4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)lo);
+          const shortx4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)hi);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], acc[mb], 0, 0, 0);
         }
       }
     }
   }
 
   // ---- epilogue ---------------------------------------------------------
-  const float lt = l + __shfl_xor(l, 32);
-  const float inv = 1.0f / lt;
+  const float inv = 1.0f / xhalf_sum(l);
   if (qvalid) {
     uint16_t* op = p.o + head_off + (int64_t)qrow * p.stride_tok;
 #pragma unroll
@@ -292,7 +362,7 @@ __global__ __launch_bounds__(2 * BLK) void fwd_kernel(const LaunchParams p) {  /
       }
   }
   if constexpr (CALIB) {
-    if (wave == 0 && lane < p.ncal) p.counts[(p.wg_abs0 + L) * p.ncal + lane] = ncount;
+    if (wave == 0 && lane < ncal) p.counts[(p.wg_abs0 + L) * ncal + lane] = ncount;
     if (tid == 0) p.tiles[p.wg_abs0 + L] = nK;
   } else {
     if (tid == 0) {
