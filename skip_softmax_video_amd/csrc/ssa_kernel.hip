@@ -291,7 +291,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
       if (lane < ncal) ncount += ((all >> lane) & 1ull) ? 0 : 1;
       keep = true;
     } else {
-      keep = all != 0;
+      keep = __builtin_amdgcn_readfirstlane(all != 0 ? 1 : 0) != 0;  // work-group uniform
       skipped += keep ? 0 : 1;
       if (p.tile_mask != nullptr && tid == 0)
         p.tile_mask[((int64_t)((p.seq_abs0 + b) * H + h) * p.mask_nq + qb) * p.mask_nk + j] = keep ? 0 : 1;
