@@ -158,6 +158,22 @@ __device__ __forceinline__ bf16x8 read_k(const uint16_t* k_lds, int kb, int s, i
   return *reinterpret_cast<const bf16x8*>(k_lds + gran * 8);
 }
 
+// A operand of O^T += V^T P^T for 16-key step s, d block mb: two transposing
+// LDS reads give lane l the 8 keys (in the permuted slot order shared with
+// P) of column d = 32 mb + l % 32.
+template <class SH>
+__device__ __forceinline__ bf16x8 read_vt(const uint16_t* v_lds, int s, int mb, int tr_row, int tr_chunk,
+                                          int tr_elem) {
+  const int r_lo = 16 * s + tr_row;
+  const int r_hi = r_lo + 8;
+  const int c = 4 * mb + tr_chunk;
+  const uint16_t* lo = v_lds + (r_lo * SH::CH + (c ^ swz_v<SH::CH>(r_lo))) * 8 + tr_elem;
+  const uint16_t* hi = v_lds + (r_hi * SH::CH + (c ^ swz_v<SH::CH>(r_hi))) * 8 + tr_elem;
+  const shortx4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)lo);
+  const shortx4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)hi);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 __device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
 template <int D, int BLK, bool CALIB>
@@ -253,6 +269,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
 #pragma unroll
       for (int kb = 0; kb < SH::KB; ++kb)
         sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s & 1][kb], qf[s], sc[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (nvalid < BLK) {
 #pragma unroll
@@ -329,20 +346,24 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
 
     if (keep) {
       // ---- O^T += V_j^T P^T ----------------------------------------------
+      // V^T operands are read two 16-key steps ahead of their MFMAs (3-deep
+      // register ring, fully unrolled); sched_barrier keeps the schedule.
+      bf16x8 va[3][SH::MB];
+#pragma unroll
+      for (int s = 0; s < 2 && s < SH::KS; ++s)
+#pragma unroll
+        for (int mb = 0; mb < SH::MB; ++mb) va[s][mb] = read_vt<SH>(v_lds, s, mb, tr_row, tr_chunk, tr_elem);
 #pragma unroll
       for (int s = 0; s < SH::KS; ++s) {
-        const int r_lo = 16 * s + tr_row;
-        const int r_hi = r_lo + 8;
+        if (s + 2 < SH::KS) {
 #pragma unroll
-        for (int mb = 0; mb < SH::MB; ++mb) {
-          const int c = 4 * mb + tr_chunk;
-          const uint16_t* lo = v_lds + (r_lo * SH::CH + (c ^ swz_v<SH::CH>(r_lo))) * 8 + tr_elem;
-          const uint16_t* hi = v_lds + (r_hi * SH::CH + (c ^ swz_v<SH::CH>(r_hi))) * 8 + tr_elem;
-          const shortx4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)lo);
-          const shortx4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)hi);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s], acc[mb], 0, 0, 0);
+          for (int mb = 0; mb < SH::MB; ++mb)
+            va[(s + 2) % 3][mb] = read_vt<SH>(v_lds, s + 2, mb, tr_row, tr_chunk, tr_elem);
         }
+#pragma unroll
+        for (int mb = 0; mb < SH::MB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s % 3][mb], pb[s], acc[mb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
