@@ -17,6 +17,7 @@ Prints one JSON line. `python bench.py --gpus 1 --steps K --warmup W`.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -30,6 +31,17 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 TARGET_SPARSITY = 0.7
 CALIB_LAMBDAS_N = 16
+KERNEL_SOURCE = os.path.join(ROOT, "skip_softmax_video_amd", "csrc", "ssa_kernel.hip")
+
+# HBM traffic of one calibrated-lambda forward launch at the headline shape,
+# from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) over
+# `bench.py --steps 2 --warmup 0 --no-cpu-baseline --copy-probe-mib 1024`,
+# each scaled by the same counter's reading for a plain 1 GiB device copy.
+# Valid only for the kernel code it was taken on (sha256 of the source without
+# comments, below); reported
+# as null once the kernel changes.
+TRAFFIC = {"kernel_sha256": "6b0f4d1f0ee0a0ca2f061e75c98832be4cb16021acb2cde3d52a29062e5f4010",
+           "fetch_bytes": 242219189095, "write_bytes": 794565488}
 
 
 def log(msg: str) -> None:
@@ -50,6 +62,32 @@ def time_launches(fn, warmup: int, steps: int):
     stop.record()
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / steps
+
+
+def blas_threads() -> int:
+    """Threads numpy's BLAS actually runs with (the oracle's matmuls)."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except ImportError:
+        pass
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def kernel_digest() -> str:
+    """sha256 of the kernel source with // comments and blank lines removed."""
+    import re
+    with open(KERNEL_SOURCE, "r") as f:
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f]
+    return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
+
+
+def traffic_bytes():
+    if TRAFFIC is None or TRAFFIC["kernel_sha256"] != kernel_digest():
+        return None
+    return int(TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"])
 
 
 def cpu_baseline(x, cu, t_log2: float, block: int, budget_s: float):
@@ -79,7 +117,7 @@ def cpu_baseline(x, cu, t_log2: float, block: int, budget_s: float):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = blas_threads()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s (dense-equiv)", "cores": threads, "kind": "oracle",
             "sample": f"{done} of {nq} Q-blocks of head {h} (sequential fp64 tile loop at the calibrated "
                       f"lambda), {dt:.1f} s, numpy/BLAS threads={threads}"}
@@ -92,6 +130,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (scale for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the kernel runs on one MI355X; multi-GPU sharding is not "
@@ -158,6 +198,17 @@ def main() -> int:
     log("timing calibrated mode")
     sparse_ms = time_launches(fwd(lam07), args.warmup, args.steps)
 
+    # context points (not the headline): the resolved 0.5 target and lambda = 1
+    sweep = []
+    for tag, lam in (("target 0.5", resolved["0.5"]["lambda"]), ("lambda 1", 1.0)):
+        ssa.attn_fwd(dx["q"], dx["k"], dx["v"], cu, lam, block=blk, out=o, skipped=skipped, total=total)
+        torch.cuda.synchronize()
+        sp_l = float(skipped.sum()) / float(total.sum())
+        ms_l = time_launches(fwd(lam), 1, max(2, args.steps // 2))
+        sweep.append({"point": tag, "lambda": lam, "achieved_tile_sparsity": round(sp_l, 4), "ms": round(ms_l, 3),
+                      "speedup_vs_dense": round(dense_ms / ms_l, 3)})
+        log(f"{tag}: lambda {lam:.4g} sparsity {sp_l:.4f} {ms_l:.2f} ms")
+
     dense_flops = cfg.dense_flops()
     exec_flops = dense_flops / 2 * (2 - s_ach)
     value = dense_flops / (sparse_ms * 1e-3) / 1e12
@@ -183,12 +234,23 @@ def main() -> int:
         "dense": {"ms": round(dense_ms, 3), "tflops": round(dense_tf, 2),
                   "frac_of_peak": round(dense_tf / PEAK_BF16_TFLOPS, 4)},
         "executed_tflops": round(exec_tf, 2),
+        "sweep": sweep,
         "calibration": {"pass_ms": round(calib_ms, 3), "fit_resolve_host_ms": round(host_ms, 3),
                         "a": fit.a, "b": fit.b, "s_min": fit.s_min, "s_max": fit.s_max,
                         "n_used": fit.n_used, "resolved": resolved},
         "roofline": {"bound": "mfma", "achieved": round(exec_tf, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(exec_tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(exec_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_bytes(), "traffic_unit": "HBM bytes per launch (read + write)"},
     }
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n} bytes read, {n} bytes written")
+        del src, dst
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(x, cu, math.log2(lam07), blk, args.cpu_budget)

@@ -28,12 +28,13 @@
 //     rescaled lazily: the exponent base only moves when some row's maximum
 //     rose by more than 2^8, which keeps P <= 256 and the result unchanged
 //     up to rounding.
-//   * K and V tiles go global -> LDS with global_load_lds_dwordx4 (no
+//   * K and V tiles go global -> LDS with buffer_load_dwordx4 ... lds (no
 //     register staging). Each wave instruction fills 1 KB of LDS; the
 //     16-byte granules of a row are XOR-swizzled so that the MFMA operand
 //     reads (ds_read_b128 for K, ds_read_b64_tr_b16 for V) avoid bank
-//     conflicts. Rows past the end of a sequence re-read the last valid row
-//     (finite values): their scores are masked to -inf and their P is 0.
+//     conflicts. Rows past the end of a sequence fall outside the buffer
+//     descriptor's range and read as zero: their scores are masked to -inf
+//     and their P is 0.
 //   * Skip vote: every lane forms x = rowmax * sm_scale * log2(e) - m for its
 //     query (m = running max before the tile; -inf on the first tile, so x =
 //     +inf and the first tile is always kept). A wave keeps the tile if any
