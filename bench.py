@@ -176,6 +176,16 @@ def main() -> int:
                                             s_max=fit.s_max)
         resolved[str(tgt)] = {"lambda": lam, "log2": t2, "status": ssa.status_string(st)}
     host_ms = (time.perf_counter() - t0) * 1e3
+    # timestep / layer gating of a 40-step flow schedule (host helper feeding the per-layer threshold)
+    t0 = time.perf_counter()
+    sched = ssa.flow_timesteps(40, 1000, 3.0)
+    gate_rules = [ssa.gate_layer("transformer.blocks.%d.attn1" % (i % 40), [sched[i]], 1.0, cutoff=0.86,
+                                 ignore=["blocks.0.attn1"])[0] for i in range(40)]
+    gate_us = (time.perf_counter() - t0) * 1e6 / 41
+    gating = {"schedule": "40-step flow, T=1000, shift 3", "cutoff": 0.86,
+              "dense_steps": ssa.gate_dense_steps(sched, 0.86),
+              "sparse_forwards": sum(1 for r in gate_rules if r == ssa.GATE_BASE),
+              "host_us_per_call": round(gate_us, 2)}
     lam07 = resolved[str(TARGET_SPARSITY)]["lambda"]
     log(f"fit a={fit.a:.4g} b={fit.b:.4g} range [{fit.s_min:.3f}, {fit.s_max:.3f}] -> lambda(0.7)={lam07:.4g}")
     del dc, out, counts, tiles
@@ -235,6 +245,7 @@ def main() -> int:
                   "frac_of_peak": round(dense_tf / PEAK_BF16_TFLOPS, 4)},
         "executed_tflops": round(exec_tf, 2),
         "sweep": sweep,
+        "gating": gating,
         "calibration": {"pass_ms": round(calib_ms, 3), "fit_resolve_host_ms": round(host_ms, 3),
                         "a": fit.a, "b": fit.b, "s_min": fit.s_min, "s_max": fit.s_max,
                         "n_used": fit.n_used, "resolved": resolved},

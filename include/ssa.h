@@ -211,6 +211,59 @@ typedef struct ssa_threshold_spec {
 int ssa_resolve_threshold(const ssa_threshold_spec* spec, int64_t seq_k, double* lambda,
                           double* log2_lambda);
 
+/* ---- timestep and layer gating (host) ---------------------------------- */
+/* Which attention forwards of a denoising run use skip-softmax, and with what
+ * scale factor ([DOCS] "Checkpoint Config", "User Configuration", "Mapping
+ * disabled_until_timestep to Actual Denoising Steps"; [TRTLLM] "Use Cases"
+ * 1d). All pointers are host; no GPU work. Patterns are fnmatch(3) patterns
+ * (case-sensitive, no backslash escapes: *, ?, [...], [!...]) matched against
+ * the full module name and against its component-relative name (the name
+ * without its first dotted component), so "blocks.0.attn1" matches
+ * "transformer.blocks.0.attn1" and "transformer_2.blocks.0.attn1". */
+#define SSA_GATE_BASE     0  /* base scale factor applies                      */
+#define SSA_GATE_TIMESTEP 1  /* dense: forward timestep >= the cutoff           */
+#define SSA_GATE_IGNORED  2  /* dense: layer matches an ignore pattern          */
+#define SSA_GATE_OVERRIDE 3  /* first matching per-layer override (0 = dense)   */
+
+typedef struct ssa_layer_override {
+  const char* pattern;  /* fnmatch pattern                                 */
+  double scale_factor;  /* threshold_scale_factor for matching layers; 0 = dense */
+} ssa_layer_override;
+
+typedef struct ssa_gate_spec {
+  double disabled_until_timestep;      /* NaN = no cutoff; else in [0, 1]           */
+  const char* const* ignore;           /* n_ignore patterns (NULL when n_ignore 0)  */
+  int32_t n_ignore;
+  const ssa_layer_override* overrides; /* n_overrides entries, first match wins     */
+  int32_t n_overrides;
+} ssa_gate_spec;
+
+/* Effective threshold_scale_factor of layer `layer` for one forward whose
+ * normalized timesteps are timesteps[0..n_timesteps) (per-token timesteps
+ * reduce to their largest value). Rules in order: dense while that timestep
+ * >= disabled_until_timestep (equality is dense); dense when an ignore pattern
+ * matches; the first matching override; else base_scale_factor. Writes
+ * *scale_factor (0 = dense) and *rule (SSA_GATE_*). The result feeds
+ * ssa_attn_fwd with SSA_THRESH_SCALE_FACTOR (lambda = sf / S_b).
+ * Errors: SSA_ERR_INVALID_ARG (NULL, n_timesteps < 1, NaN timestep, cutoff
+ * outside [0, 1], negative or NaN scale factors). */
+int ssa_gate_layer(const ssa_gate_spec* g, const char* layer, const double* timesteps,
+                   int32_t n_timesteps, double base_scale_factor, double* scale_factor, int32_t* rule);
+
+/* Normalized runtime timesteps of an n_steps flow-matching schedule with
+ * num_train_timesteps T and flow shift f:
+ * s[i] = 1 - i (1 - 1/T) / n_steps, shifted = f s / (1 + (f - 1) s),
+ * t[i] = (1 - 1/T) shifted ([DOCS] "Mapping disabled_until_timestep to
+ * Actual Denoising Steps", 40-step example with T = 1000, f = 3; the final
+ * (1 - 1/T) factor is this library's reading of the unprinted conversion to
+ * runtime timesteps, chosen because it reproduces the printed table).
+ * Errors: SSA_ERR_INVALID_ARG (NULL, n_steps < 1, T < 1, f <= 0 or NaN). */
+int ssa_flow_timesteps(int32_t n_steps, int32_t num_train_timesteps, double flow_shift, double* t);
+
+/* dense_steps = count(t[i] >= cutoff) over t[0..n); cutoff NaN gives 0.
+ * Errors: SSA_ERR_INVALID_ARG (NULL, n < 0, cutoff outside [0, 1]). */
+int ssa_gate_dense_steps(const double* t, int32_t n, double cutoff, int32_t* dense_steps);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char* ssa_status_string(int status);
 

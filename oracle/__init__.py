@@ -12,8 +12,10 @@ Contents:
                    counter and the textbook dense attention definition.
   calibration   -- log2 threshold conversion, the log-space exponential fit,
                    threshold resolution with its priority rules.
+  gating        -- flow-schedule timesteps, the disabled_until_timestep
+                   cutoff and per-layer ignore / override patterns.
 
 Parity status of every function is stated in its docstring ("pinned by ..."
 or "parity unpinned").
 """
-from . import calibration, skip_softmax  # noqa: F401
+from . import calibration, gating, skip_softmax  # noqa: F401

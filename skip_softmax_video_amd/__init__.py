@@ -6,6 +6,10 @@ package is its thin Python binding. Build the library with
 """
 from ._binding import (  # noqa: F401
     EXPORTED,
+    GATE_BASE,
+    GATE_IGNORED,
+    GATE_OVERRIDE,
+    GATE_TIMESTEP,
     SSA_ERR_FIT_DEGENERATE,
     SSA_ERR_HIP,
     SSA_ERR_INVALID_ARG,
@@ -20,6 +24,9 @@ from ._binding import (  # noqa: F401
     calib_num_workgroups,
     calibration_fit,
     calibration_sparsity,
+    flow_timesteps,
+    gate_dense_steps,
+    gate_layer,
     load_library,
     make_problem,
     resolve_threshold,

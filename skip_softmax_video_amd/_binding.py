@@ -43,7 +43,13 @@ SPEC_RANGE = 1 << 7
 EXPORTED = (
     "ssa_attn_fwd", "ssa_tile_mask_dims", "ssa_attn_calibrate", "ssa_calib_num_workgroups",
     "ssa_calibration_sparsity", "ssa_calibration_fit", "ssa_resolve_threshold", "ssa_status_string",
+    "ssa_gate_layer", "ssa_flow_timesteps", "ssa_gate_dense_steps",
 )
+
+GATE_BASE = 0
+GATE_TIMESTEP = 1
+GATE_IGNORED = 2
+GATE_OVERRIDE = 3
 
 
 class SSAError(RuntimeError):
@@ -76,6 +82,16 @@ class ThresholdSpec(ctypes.Structure):
                 ("s_min", ctypes.c_double), ("s_max", ctypes.c_double)]
 
 
+class LayerOverride(ctypes.Structure):
+    _fields_ = [("pattern", ctypes.c_char_p), ("scale_factor", ctypes.c_double)]
+
+
+class GateSpec(ctypes.Structure):
+    _fields_ = [("disabled_until_timestep", ctypes.c_double), ("ignore", ctypes.POINTER(ctypes.c_char_p)),
+                ("n_ignore", ctypes.c_int32), ("overrides", ctypes.POINTER(LayerOverride)),
+                ("n_overrides", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -98,6 +114,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ssa_calibration_sparsity": [P(Problem), P(i32), P(i32), i32, P(dbl)],
         "ssa_calibration_fit": [P(dbl), P(dbl), P(dbl), i32, P(CalibResult)],
         "ssa_resolve_threshold": [P(ThresholdSpec), i64, P(dbl), P(dbl)],
+        "ssa_gate_layer": [P(GateSpec), ctypes.c_char_p, P(dbl), i32, dbl, P(dbl), P(i32)],
+        "ssa_flow_timesteps": [i32, i32, dbl, P(dbl)],
+        "ssa_gate_dense_steps": [P(dbl), i32, dbl, P(i32)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -259,3 +278,40 @@ def resolve_threshold(seq_k: int, raw_log2=None, lam=None, scale_factor=None, ta
     st = load_library().ssa_resolve_threshold(ctypes.byref(spec), int(seq_k), ctypes.byref(out_l), ctypes.byref(out_t))
     _check(st, "ssa_resolve_threshold")
     return st, out_l.value, out_t.value
+
+
+# ---- timestep and layer gating (host) -----------------------------------------
+def gate_layer(layer: str, timesteps, base_scale_factor: float, cutoff: Optional[float] = None,
+               ignore: Sequence[str] = (), overrides: Sequence[Tuple[str, float]] = ()) -> Tuple[int, float]:
+    """ssa_gate_layer: (rule, effective threshold_scale_factor) of one layer at one forward."""
+    ts = np.ascontiguousarray(np.atleast_1d(np.asarray(timesteps, dtype=np.float64)))
+    ign = (ctypes.c_char_p * max(1, len(ignore)))(*[p.encode() for p in ignore])
+    ovr = (LayerOverride * max(1, len(overrides)))(*[LayerOverride(p.encode(), float(v)) for p, v in overrides])
+    spec = GateSpec(disabled_until_timestep=float("nan") if cutoff is None else float(cutoff),
+                    ignore=ign, n_ignore=len(ignore), overrides=ovr, n_overrides=len(overrides))
+    sf, rule = ctypes.c_double(), ctypes.c_int32()
+    _check(load_library().ssa_gate_layer(ctypes.byref(spec), layer.encode(),
+                                         ts.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), ts.size,
+                                         float(base_scale_factor), ctypes.byref(sf), ctypes.byref(rule)),
+           "ssa_gate_layer")
+    return rule.value, sf.value
+
+
+def flow_timesteps(n_steps: int, num_train_timesteps: int = 1000, flow_shift: float = 3.0) -> np.ndarray:
+    """ssa_flow_timesteps: normalized runtime timesteps of an n-step flow schedule."""
+    t = np.empty(max(0, n_steps), dtype=np.float64)
+    _check(load_library().ssa_flow_timesteps(int(n_steps), int(num_train_timesteps), float(flow_shift),
+                                             t.ctypes.data_as(ctypes.POINTER(ctypes.c_double))),
+           "ssa_flow_timesteps")
+    return t
+
+
+def gate_dense_steps(timesteps, cutoff: Optional[float]) -> int:
+    """ssa_gate_dense_steps: count(t >= cutoff); None = no cutoff."""
+    ts = np.ascontiguousarray(np.asarray(timesteps, dtype=np.float64))
+    n = ctypes.c_int32()
+    _check(load_library().ssa_gate_dense_steps(ts.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), ts.size,
+                                               float("nan") if cutoff is None else float(cutoff),
+                                               ctypes.byref(n)),
+           "ssa_gate_dense_steps")
+    return n.value

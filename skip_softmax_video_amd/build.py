@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libssa.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["ssa_kernel.hip", "ssa_host.cpp"]
+SOURCES = ["ssa_kernel.hip", "ssa_host.cpp", "ssa_gate.cpp"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for every HIP translation unit.
@@ -34,7 +34,7 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile ssa_kernel.hip + ssa_host.cpp into libssa.so; return its path."""
+    """Compile the HIP kernels and the host sources into libssa.so; return its path."""
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]

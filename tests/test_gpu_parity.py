@@ -230,3 +230,36 @@ def test_wan5b_sampled_parity():
 def test_headline_sampled_parity():
     fr = _sampled_parity(CONFIGS["headline"], [0.0, 8e-3], heads=[0, 19, 39], per_head=3)
     assert fr[0] == 0.0 and fr[1] > 0.3
+
+
+def test_denoising_schedule_gating():
+    """Gating feeds the forward: over a 40-step flow schedule with cutoff 0.86,
+    the first 14 forwards run dense and the rest skip exactly the oracle's
+    tiles at lambda = sf / S (sf from the layer's override)."""
+    import skip_softmax_video_amd as ssa
+    from oracle import gating as og
+    cfg = CONFIGS["tiny"]
+    x, xd, cu = _inputs(cfg)
+    xf = _f64(x)
+    S, H = int(cu[1]), cfg.num_heads
+    sched = ssa.flow_timesteps(40, 1000, 3.0)
+    layer, cutoff = "transformer.blocks.3.attn1", 0.86
+    ovr = [("blocks.3.*", 0.1 * S)]  # lambda = 0.1 for this layer
+    lam_ref = og.gate_layer(layer, [0.0], 0.0, cutoff, (), ovr)[1] / S
+    t_ref = np.full((1, H), math.log2(lam_ref))
+    ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t_ref, cfg.block)
+    dense_ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, np.full((1, H), -math.inf), cfg.block)
+    n_dense = 0
+    for i, t in enumerate(sched):
+        rule, sf = ssa.gate_layer(layer, [t], 0.0, cutoff, ["blocks.0.attn1"], ovr)
+        assert (rule, sf) == og.gate_layer(layer, [t], 0.0, cutoff, ["blocks.0.attn1"], ovr)
+        o, sk, tot, mask = gpu_forward(xd, cu, sf, "scale_factor", cfg.block)
+        if rule == ssa.GATE_TIMESTEP:
+            n_dense += 1
+            assert sk.sum() == 0
+            compare_outputs(o, dense_ref["o"])
+        else:
+            compare_masks(mask, ref, t_ref, osk.workgroups(cu, H, cfg.block))
+            assert sk.sum() > 0
+    assert n_dense == 14
+    log(f"  40 forwards: {n_dense} dense, {40 - n_dense} skip-softmax")

@@ -181,3 +181,57 @@ def test_status_strings():
     for code in (0, 1, -1, -2, -3, -4, -5, -6):
         assert ssa.status_string(code) and ssa.status_string(code) != "unknown status"
     assert ssa.status_string(99) == "unknown status"
+
+
+# ---- timestep and layer gating --------------------------------------------------
+from oracle import gating as og  # noqa: E402
+
+
+@pytest.mark.parametrize("n,T,shift", [(40, 1000, 3.0), (50, 1000, 5.0), (1, 1000, 3.0), (30, 1, 1.0),
+                                       (7, 20, 0.5)])
+def test_flow_timesteps_match_oracle(n, T, shift):
+    got = ssa.flow_timesteps(n, T, shift)
+    ref = og.flow_timesteps(n, T, shift)
+    assert np.allclose(got, ref, rtol=0, atol=1e-15)
+
+
+def test_gate_dense_steps_match_oracle(golden):
+    g = golden("unipc_40_steps.txt")
+    t = ssa.flow_timesteps(40, 1000, 3.0)
+    for c, d in zip(g["cutoffs"][0], g["dense_steps"][0]):
+        assert ssa.gate_dense_steps(t, c) == og.dense_steps(t, c) == int(d)
+    assert ssa.gate_dense_steps(t, None) == 0 and ssa.gate_dense_steps(t, 0.0) == 40
+    assert ssa.gate_dense_steps([], 0.5) == 0
+
+
+_NAMES = ["transformer.blocks.0.attn1", "transformer_2.blocks.0.attn1", "transformer.blocks.10.attn1",
+          "blocks.0.attn2", "single_transformer_blocks.3.attn", "transformer_blocks.0.attn",
+          "transformer_blocks.12.attn", "attn", "a.b.c.d"]
+_PATTERNS = ["blocks.0.attn1", "blocks.0.*", "*attn2", "transformer_blocks.0*", "single_transformer_blocks*",
+             "blocks.?.attn1", "blocks.[01].attn1", "blocks.[!0].attn1", "*", "b.c.*", "a.b.c.d", "nomatch"]
+
+
+def test_gate_layer_matches_oracle():
+    rng = np.random.default_rng(5)
+    for _ in range(400):
+        name = _NAMES[rng.integers(len(_NAMES))]
+        ign = [_PATTERNS[i] for i in rng.choice(len(_PATTERNS), rng.integers(0, 3), replace=False)]
+        ovr = [(_PATTERNS[i], float(rng.choice([0.0, 800.0, 8000.0])))
+               for i in rng.choice(len(_PATTERNS), rng.integers(0, 4), replace=False)]
+        cutoff = [None, 0.0, 0.6, 0.86, 1.0][rng.integers(5)]
+        ts = rng.uniform(0, 1, rng.integers(1, 4))
+        base = float(rng.choice([0.0, 5000.0, 123.5]))
+        assert ssa.gate_layer(name, ts, base, cutoff, ign, ovr) == og.gate_layer(name, ts, base, cutoff, ign, ovr)
+
+
+@pytest.mark.parametrize("kw", [dict(cutoff=1.5), dict(cutoff=-0.1), dict(base=-1.0), dict(base=math.nan),
+                                dict(ts=[math.nan]), dict(ts=[]), dict(ovr=[("x", -2.0)])])
+def test_gate_errors(kw):
+    with pytest.raises(ssa.SSAError) as e:
+        ssa.gate_layer("a.b", kw.get("ts", [0.5]), kw.get("base", 1.0), kw.get("cutoff"), (), kw.get("ovr", ()))
+    assert e.value.status == ssa.SSA_ERR_INVALID_ARG
+    for bad in (dict(n=0), dict(T=0), dict(shift=0.0), dict(shift=math.nan)):
+        with pytest.raises(ssa.SSAError):
+            ssa.flow_timesteps(bad.get("n", 4), bad.get("T", 1000), bad.get("shift", 3.0))
+    with pytest.raises(ssa.SSAError):
+        ssa.gate_dense_steps([0.5], 2.0)
