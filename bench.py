@@ -170,6 +170,7 @@ def main() -> int:
     t0 = time.perf_counter()
     sp = ssa.calibration_sparsity(cu, H, D, blk, counts.cpu().numpy(), tiles.cpu().numpy())[0]
     fit = ssa.calibration_fit(lams, sp, float(S))
+    fit_lin = ssa.calibration_fit(lams, sp, float(S), space="linear")
     resolved = {}
     for tgt in (0.25, 0.5, 0.7):
         st, lam, t2 = ssa.resolve_threshold(S, target_sparsity=tgt, a=fit.a, b=fit.b, s_min=fit.s_min,
@@ -248,7 +249,8 @@ def main() -> int:
         "gating": gating,
         "calibration": {"pass_ms": round(calib_ms, 3), "fit_resolve_host_ms": round(host_ms, 3),
                         "a": fit.a, "b": fit.b, "s_min": fit.s_min, "s_max": fit.s_max,
-                        "n_used": fit.n_used, "resolved": resolved},
+                        "n_used": fit.n_used, "resolved": resolved,
+                        "fit_linear": {"a": fit_lin.a, "b": fit_lin.b}},
         "roofline": {"bound": "mfma", "achieved": round(exec_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(exec_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes(), "traffic_unit": "HBM bytes per launch (read + write)"},

@@ -176,6 +176,47 @@ typedef struct ssa_calib_result {
 int ssa_calibration_fit(const double* lambda, const double* sparsity, const double* seq_k,
                         int32_t n, ssa_calib_result* out);
 
+/* Linear-space variant of the fit: minimises sum_i (a e^{b s_i} - y_i)^2 with
+ * y_i = lambda_i * seq_k_i over the same usable points ([TRITON]
+ * "Calibration" / "Config & conversion": fit_logspace = False is the
+ * calibrator's default, the log-space fit the recommended one for
+ * diffusion). For fixed b the best a is closed-form, so b maximises
+ * H(b) = (sum y e^{bs})^2 / sum e^{2bs}. The search scans b over the
+ * log-space slope +- 100 in steps of 0.1, then bisects dH/db = 0 around the
+ * best grid point. Errors: SSA_ERR_INVALID_ARG, SSA_ERR_FIT_DEGENERATE (also
+ * when the optimum lies at the edge of the scan). */
+int ssa_calibration_fit_linear(const double* lambda, const double* sparsity, const double* seq_k,
+                               int32_t n, ssa_calib_result* out);
+
+/* Calibration counts pooled over passes, one group per key length
+ * (multi-sample accumulation: samples of one shape share a group;
+ * multi-shape calibration: each resolution keeps its own group, see [README]
+ * "Known Issues", resolution-dependent fit). The caller owns the arrays and
+ * sets n_groups = 0 (and n_lambda = 0 or the pass's n) before the first add.
+ * Every pass added must use the same threshold list. */
+typedef struct ssa_calib_pool {
+  int32_t n_lambda;    /* thresholds per pass; 0 = take the first pass's n          */
+  int32_t max_groups;  /* capacity of the arrays below                               */
+  int32_t n_groups;    /* groups in use, in order of first appearance                */
+  int64_t* seq_k;      /* [max_groups] key length of each group                      */
+  int64_t* skipped;    /* [max_groups * n_lambda] skipped tiles per threshold        */
+  int64_t* visited;    /* [max_groups] visited tiles                                 */
+} ssa_calib_pool;
+
+/* Add one calibration pass (HOST copies of its counts [num_wg, n] and tiles
+ * [num_wg]) to the pool: sequence b's work-groups go to the group of key
+ * length S_b; empty sequences are ignored. Errors: SSA_ERR_INVALID_ARG (also
+ * n != pool->n_lambda, or more key lengths than max_groups; the pool is then
+ * unchanged). */
+int ssa_calibration_pool_add(const ssa_problem* p, const int32_t* counts, const int32_t* tiles,
+                             int32_t n, ssa_calib_pool* pool);
+
+/* Fit points of the pool, group-major: point g * n_lambda + k is
+ * (lambdas[k], skipped[g][k] / visited[g], seq_k[g]); writes
+ * n_groups * n_lambda points to each output array. */
+int ssa_calibration_pool_points(const ssa_calib_pool* pool, const double* lambdas, double* lambda_out,
+                                double* sparsity_out, double* seq_k_out, int32_t* n_points);
+
 /* ---- threshold resolution ---------------------------------------------- */
 /* Resolve the user/checkpoint threshold sources into lambda and log2(lambda)
  * for a sequence of seq_k keys. Fields are read only when their flag is set

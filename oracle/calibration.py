@@ -24,7 +24,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -81,6 +81,109 @@ def fit_exponential_logspace(lambdas: Sequence[float], sparsities: Sequence[floa
     log_a = float(ym - b * xm)
     return Fit(a=math.exp(log_a), log_a=log_a, b=b, s_min=float(x.min()), s_max=float(x.max()),
                n_used=int(x.size))
+
+
+def _usable_points(lambdas, sparsities, seq_k):
+    lam = np.asarray(lambdas, np.float64)
+    s = np.asarray(sparsities, np.float64)
+    sk = np.broadcast_to(np.asarray(seq_k, np.float64), lam.shape)
+    use = (s > 0.0) & (s < 1.0) & (lam > 0.0)
+    return s[use], lam[use] * sk[use]
+
+
+def fit_exponential_linear(lambdas: Sequence[float], sparsities: Sequence[float],
+                           seq_k: Sequence[float]) -> Fit:
+    """Least-squares fit of scale_factor = a * exp(b * sparsity) in linear space.
+
+    This is the calibrator's non-log option: fit_logspace = False, the
+    ModelOpt default; the log-space fit is the one recommended for diffusion.
+    It minimises sum_i (a e^{b s_i} - y_i)^2 with y_i = lambda_i * seq_k_i,
+    over the same usable points as the log-space fit.
+
+    For a fixed b the best a is closed-form:
+        a(b) = sum y e^{bs} / sum e^{2bs}.
+    So the fit maximises H(b) = (sum y e^{bs})^2 / sum e^{2bs}. This is done
+    by a grid over b0 +- 100 in steps of 0.1 (b0 is the log-space slope), then
+    the root of dH/db inside the two cells around the best grid point, found
+    with scipy's brentq. Raises ValueError for degenerate data, or when the
+    maximiser lies at the edge of the grid.
+
+    Pinned by:
+    - exact recovery of (a, b) from points on a known curve;
+    - the zero gradient of the squared error at the returned (a, b);
+    - scipy.optimize.curve_fit on noisy points (tests).
+    """
+    from scipy.optimize import brentq
+
+    x, y = _usable_points(lambdas, sparsities, seq_k)
+    if x.size < 2 or np.unique(x).size < 2:
+        raise ValueError("degenerate fit: fewer than two distinct usable sparsities")
+    b0 = fit_exponential_logspace(lambdas, sparsities, seq_k).b
+    xc = x - float(x.max())  # H is invariant to scaling u by e^{-b max(x)}
+
+    def h(b):
+        u = np.exp(b * xc)
+        return np.sum(y * u) ** 2 / np.sum(u * u)
+
+    def dh_sign(b):  # sign of dH/db: 2 N' D - N D' with N = sum y u, D = sum u^2
+        u = np.exp(b * xc)
+        n, d = np.sum(y * u), np.sum(u * u)
+        return 2.0 * np.sum(y * xc * u) * d - n * 2.0 * np.sum(xc * u * u)
+
+    grid = b0 + np.linspace(-100.0, 100.0, 2001)
+    k = int(np.argmax([h(b) for b in grid]))
+    if k == 0 or k == grid.size - 1:
+        raise ValueError("degenerate fit: the linear-space optimum is not interior")
+    lo, hi = grid[k - 1], grid[k + 1]
+    b = float(brentq(dh_sign, lo, hi, xtol=1e-15, rtol=1e-15, maxiter=500))
+    u = np.exp(b * xc)
+    log_a = math.log(np.sum(y * u) / np.sum(u * u)) - b * float(x.max())
+    return Fit(a=math.exp(log_a), log_a=log_a, b=b, s_min=float(x.min()), s_max=float(x.max()),
+               n_used=int(x.size))
+
+
+class CalibPool:
+    """Calibration counts pooled over passes, one group per key length.
+
+    Several samples of one shape pool into one group (multi-sample
+    accumulation). Different shapes keep separate groups, whose points can be
+    fitted together or apart. This addresses the resolution dependence the
+    README lists under "Known Issues".
+
+    Group sparsity at threshold k = sum of skipped tiles / sum of visited
+    tiles over every sequence of that key length. This is the same
+    tile-weighted ratio as one pass over all of those sequences.
+
+    Pinned by: pooling two passes equals one pass over the union of their
+    work-groups (tests).
+    """
+
+    def __init__(self, n_lambda: int):
+        self.n_lambda = int(n_lambda)
+        self.groups: Dict[int, List] = {}  # seq_k -> [skipped (n_lambda,), visited]; insertion order kept
+
+    def add(self, counts, tiles, cu_seqlens, num_heads: int, block: int) -> None:
+        counts = np.asarray(counts, np.int64).reshape(-1, self.n_lambda)
+        tiles = np.asarray(tiles, np.int64).reshape(-1)
+        w = 0
+        for b in range(len(cu_seqlens) - 1):
+            S = int(cu_seqlens[b + 1]) - int(cu_seqlens[b])
+            nwg = -(-S // block) * num_heads
+            if S > 0:
+                g = self.groups.setdefault(S, [np.zeros(self.n_lambda, np.int64), 0])
+                g[0] = g[0] + counts[w:w + nwg].sum(axis=0)
+                g[1] += int(tiles[w:w + nwg].sum())
+            w += nwg
+
+    def points(self, lambdas: Sequence[float]) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """Flattened fit points (lambda, sparsity, seq_k), group-major."""
+        lam, sp, sk = [], [], []
+        for S, (skipped, visited) in self.groups.items():
+            for k in range(self.n_lambda):
+                lam.append(float(lambdas[k]))
+                sp.append(skipped[k] / visited)
+                sk.append(float(S))
+        return np.array(lam), np.array(sp), np.array(sk)
 
 
 @dataclasses.dataclass

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     SSA_ERR_UNSUPPORTED,
     SSA_OK,
     SSA_WARN_EXTRAPOLATED,
+    CalibrationPool,
     SSAError,
     attn_calibrate,
     attn_fwd,

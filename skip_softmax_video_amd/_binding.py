@@ -44,6 +44,7 @@ EXPORTED = (
     "ssa_attn_fwd", "ssa_tile_mask_dims", "ssa_attn_calibrate", "ssa_calib_num_workgroups",
     "ssa_calibration_sparsity", "ssa_calibration_fit", "ssa_resolve_threshold", "ssa_status_string",
     "ssa_gate_layer", "ssa_flow_timesteps", "ssa_gate_dense_steps",
+    "ssa_calibration_fit_linear", "ssa_calibration_pool_add", "ssa_calibration_pool_points",
 )
 
 GATE_BASE = 0
@@ -82,6 +83,12 @@ class ThresholdSpec(ctypes.Structure):
                 ("s_min", ctypes.c_double), ("s_max", ctypes.c_double)]
 
 
+class CalibPoolC(ctypes.Structure):
+    _fields_ = [("n_lambda", ctypes.c_int32), ("max_groups", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("seq_k", ctypes.POINTER(ctypes.c_int64)), ("skipped", ctypes.POINTER(ctypes.c_int64)),
+                ("visited", ctypes.POINTER(ctypes.c_int64))]
+
+
 class LayerOverride(ctypes.Structure):
     _fields_ = [("pattern", ctypes.c_char_p), ("scale_factor", ctypes.c_double)]
 
@@ -114,6 +121,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "ssa_calibration_sparsity": [P(Problem), P(i32), P(i32), i32, P(dbl)],
         "ssa_calibration_fit": [P(dbl), P(dbl), P(dbl), i32, P(CalibResult)],
         "ssa_resolve_threshold": [P(ThresholdSpec), i64, P(dbl), P(dbl)],
+        "ssa_calibration_fit_linear": [P(dbl), P(dbl), P(dbl), i32, P(CalibResult)],
+        "ssa_calibration_pool_add": [P(Problem), P(i32), P(i32), i32, P(CalibPoolC)],
+        "ssa_calibration_pool_points": [P(CalibPoolC), P(dbl), P(dbl), P(dbl), P(dbl), P(i32)],
         "ssa_gate_layer": [P(GateSpec), ctypes.c_char_p, P(dbl), i32, dbl, P(dbl), P(i32)],
         "ssa_flow_timesteps": [i32, i32, dbl, P(dbl)],
         "ssa_gate_dense_steps": [P(dbl), i32, dbl, P(i32)],
@@ -246,18 +256,63 @@ def calibration_sparsity(cu_seqlens, num_heads: int, head_dim: int, block: int, 
     return out
 
 
-def calibration_fit(lambdas, sparsity, seq_k) -> CalibResult:
-    """ssa_calibration_fit: log-space fit of scale_factor = a * exp(b * s)."""
+def calibration_fit(lambdas, sparsity, seq_k, space: str = "log") -> CalibResult:
+    """ssa_calibration_fit (space="log") or ssa_calibration_fit_linear (space="linear"):
+    fit of scale_factor = a * exp(b * s)."""
     lam = np.ascontiguousarray(np.asarray(lambdas, dtype=np.float64))
     sp = np.ascontiguousarray(np.asarray(sparsity, dtype=np.float64))
     sk = np.ascontiguousarray(np.broadcast_to(np.asarray(seq_k, dtype=np.float64), lam.shape))
     res = CalibResult()
     P = ctypes.POINTER
-    _check(load_library().ssa_calibration_fit(lam.ctypes.data_as(P(ctypes.c_double)),
-                                              sp.ctypes.data_as(P(ctypes.c_double)),
-                                              sk.ctypes.data_as(P(ctypes.c_double)), lam.size, ctypes.byref(res)),
-           "ssa_calibration_fit")
+    name = {"log": "ssa_calibration_fit", "linear": "ssa_calibration_fit_linear"}[space]
+    _check(getattr(load_library(), name)(lam.ctypes.data_as(P(ctypes.c_double)),
+                                         sp.ctypes.data_as(P(ctypes.c_double)),
+                                         sk.ctypes.data_as(P(ctypes.c_double)), lam.size, ctypes.byref(res)),
+           name)
     return res
+
+
+class CalibrationPool:
+    """ssa_calib_pool owned from Python: add calibration passes, read fit points."""
+
+    def __init__(self, n_lambda: int, max_groups: int = 64):
+        self._seq_k = np.zeros(max_groups, dtype=np.int64)
+        self._skipped = np.zeros(max_groups * n_lambda, dtype=np.int64)
+        self._visited = np.zeros(max_groups, dtype=np.int64)
+        P = ctypes.POINTER
+        self.c = CalibPoolC(n_lambda=n_lambda, max_groups=max_groups, n_groups=0,
+                            seq_k=self._seq_k.ctypes.data_as(P(ctypes.c_int64)),
+                            skipped=self._skipped.ctypes.data_as(P(ctypes.c_int64)),
+                            visited=self._visited.ctypes.data_as(P(ctypes.c_int64)))
+
+    def add(self, cu_seqlens, num_heads: int, block: int, counts, tiles) -> None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        c = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
+        t = np.ascontiguousarray(np.asarray(tiles, dtype=np.int32))
+        P = ctypes.POINTER
+        prob = Problem(batch=len(cu) - 1, num_heads=num_heads, head_dim=128, block=block,
+                       cu_seqlens=cu.ctypes.data_as(P(ctypes.c_int32)), stride_token=num_heads * 128,
+                       stride_head=128, sm_scale=0.0)
+        _check(load_library().ssa_calibration_pool_add(ctypes.byref(prob), c.ctypes.data_as(P(ctypes.c_int32)),
+                                                       t.ctypes.data_as(P(ctypes.c_int32)), c.shape[1],
+                                                       ctypes.byref(self.c)), "ssa_calibration_pool_add")
+
+    def points(self, lambdas) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        lam = np.ascontiguousarray(np.asarray(lambdas, dtype=np.float64))
+        m = self.c.n_groups * self.c.n_lambda
+        outs = [np.empty(m, dtype=np.float64) for _ in range(3)]
+        n = ctypes.c_int32()
+        P = ctypes.POINTER
+        _check(load_library().ssa_calibration_pool_points(
+            ctypes.byref(self.c), lam.ctypes.data_as(P(ctypes.c_double)),
+            *[o.ctypes.data_as(P(ctypes.c_double)) for o in outs], ctypes.byref(n)), "ssa_calibration_pool_points")
+        return tuple(o[:n.value] for o in outs)
+
+    @property
+    def groups(self):
+        g = self.c.n_groups
+        return {int(self._seq_k[i]): (self._skipped[i * self.c.n_lambda:(i + 1) * self.c.n_lambda].copy(),
+                                      int(self._visited[i])) for i in range(g)}
 
 
 def resolve_threshold(seq_k: int, raw_log2=None, lam=None, scale_factor=None, target_sparsity=None,

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libssa.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["ssa_kernel.hip", "ssa_host.cpp", "ssa_gate.cpp"]
+SOURCES = ["ssa_kernel.hip", "ssa_host.cpp", "ssa_gate.cpp", "ssa_calib.cpp"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for every HIP translation unit.

@@ -263,3 +263,45 @@ def test_denoising_schedule_gating():
             assert sk.sum() > 0
     assert n_dense == 14
     log(f"  40 forwards: {n_dense} dense, {40 - n_dense} skip-softmax")
+
+
+def test_pooled_calibration_multi_sample_multi_shape():
+    """Two calibration passes (three sequences of 1,024 tokens and one of 512,
+    two samples) pooled by key length through the C ABI, then the log- and
+    linear-space fits, against the oracle's pool of its own counts."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    second = VideoTokenConfig("tiny_b", ((4, 16, 16), (2, 16, 16), (4, 16, 16)), num_heads=2, head_dim=64,
+                              sigma=0.5, block=64, seed=11)
+    lams = np.geomspace(1e-6, 0.7, 16)
+    ts = np.log2(lams)
+    pool = ssa.CalibrationPool(16, max_groups=4)
+    ref_pool = oc.CalibPool(16)
+    band_by_key = {}
+    for cfg in (CONFIGS["tiny"], second):
+        x, xd, cu = _inputs(cfg)
+        xf = _f64(x)
+        log(f"[{cfg.name}] calibration pass, sequences {np.diff(cu).tolist()}")
+        _, counts, tiles = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, lams, block=cfg.block)
+        torch.cuda.synchronize()
+        counts, tiles = counts.cpu().numpy(), tiles.cpu().numpy()
+        pool.add(cu, cfg.num_heads, cfg.block, counts, tiles)
+        ref = osk.calibration_counts(xf["q"], xf["k"], xf["v"], cu, ts, cfg.block)
+        ref_pool.add(ref["counts"], ref["tiles"], cu, cfg.num_heads, cfg.block)
+        d = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, -math.inf, cfg.block, fast=True)["d"]
+        for n, (b, h, i) in enumerate(osk.workgroups(cu, cfg.num_heads, cfg.block)):
+            key = int(cu[b + 1] - cu[b])
+            band_by_key.setdefault(key, np.zeros(16, np.int64))
+            band_by_key[key] += np.array([np.sum(np.abs(d[b, h, i] - t) <= 1e-3) for t in ts])
+    got, exp = pool.groups, ref_pool.groups
+    assert list(got) == list(exp) == [1024, 512]
+    for key in exp:
+        assert got[key][1] == exp[key][1]
+        assert np.all(np.abs(got[key][0] - exp[key][0]) <= band_by_key[key])
+    lam_g, sp_g, sk_g = pool.points(lams)
+    lam_r, sp_r, sk_r = ref_pool.points(lams)
+    for space, ofit in (("log", oc.fit_exponential_logspace), ("linear", oc.fit_exponential_linear)):
+        g = ssa.calibration_fit(lam_g, sp_g, sk_g, space=space)
+        r = ofit(lam_r, sp_r, sk_r)
+        log(f"  {space}: a={g.a:.5g} b={g.b:.5g} (oracle a={r.a:.5g} b={r.b:.5g}) points {g.n_used}")
+        assert g.b == pytest.approx(r.b, rel=1e-3) and g.a == pytest.approx(r.a, rel=1e-3)

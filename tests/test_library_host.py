@@ -235,3 +235,75 @@ def test_gate_errors(kw):
             ssa.flow_timesteps(bad.get("n", 4), bad.get("T", 1000), bad.get("shift", 3.0))
     with pytest.raises(ssa.SSAError):
         ssa.gate_dense_steps([0.5], 2.0)
+
+
+# ---- linear-space fit and pooled calibration -------------------------------------
+@pytest.mark.parametrize("seed", range(6))
+def test_linear_fit_matches_oracle(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(3, 30))
+    s = np.sort(rng.uniform(0.2, 0.95, n))
+    a, b = 10 ** rng.uniform(-6, 1), rng.uniform(5, 40)
+    seq_k = rng.choice([8190.0, 32760.0, 75600.0], n)
+    lam = np.minimum(a * np.exp(b * s) * np.exp(rng.normal(0, 0.25, n)) / seq_k, 1.0)
+    got = ssa.calibration_fit(lam, s, seq_k, space="linear")
+    ref = oc.fit_exponential_linear(lam, s, seq_k)
+    assert got.b == pytest.approx(ref.b, rel=1e-9)
+    assert got.a == pytest.approx(ref.a, rel=1e-9)
+    assert (got.s_min, got.s_max, got.n_used) == (ref.s_min, ref.s_max, ref.n_used)
+
+
+def test_linear_fit_degenerate():
+    with pytest.raises(ssa.SSAError) as e:
+        ssa.calibration_fit([1e-3, 1e-2], [0.5, 0.5], 100.0, space="linear")
+    assert e.value.status == ssa.SSA_ERR_FIT_DEGENERATE
+
+
+def _random_pass(rng, H, block, n, lengths):
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    nwg = sum(-(-int(S) // block) * H for S in lengths)
+    tiles = np.zeros(nwg, np.int32)
+    w = 0
+    for S in lengths:
+        nt = -(-int(S) // block)
+        tiles[w:w + nt * H] = nt
+        w += nt * H
+    counts = np.sort(rng.integers(0, np.maximum(tiles, 1)[:, None], (nwg, n)), axis=1).astype(np.int32)
+    return cu, counts, tiles
+
+
+def test_pool_matches_oracle():
+    rng = np.random.default_rng(9)
+    H, block, n = 3, 128, 5
+    lams = np.geomspace(1e-5, 0.5, n)
+    pool, ref = ssa.CalibrationPool(n, max_groups=8), oc.CalibPool(n)
+    for lengths in ([300, 1000, 0, 300], [1000], [77, 300, 129]):
+        cu, counts, tiles = _random_pass(rng, H, block, n, lengths)
+        pool.add(cu, H, block, counts, tiles)
+        ref.add(counts, tiles, cu, H, block)
+    got, exp = pool.groups, ref.groups
+    assert list(got) == list(exp) == [300, 1000, 77, 129]
+    for key in exp:
+        np.testing.assert_array_equal(got[key][0], exp[key][0])
+        assert got[key][1] == exp[key][1]
+    for a, b in zip(pool.points(lams), ref.points(lams)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_pool_errors_leave_it_unchanged():
+    rng = np.random.default_rng(3)
+    pool = ssa.CalibrationPool(4, max_groups=2)
+    cu, counts, tiles = _random_pass(rng, 2, 64, 4, [100, 200])
+    pool.add(cu, 2, 64, counts, tiles)
+    before = {k: (v[0].copy(), v[1]) for k, v in pool.groups.items()}
+    cu2, counts2, tiles2 = _random_pass(rng, 2, 64, 4, [100, 300])  # a third key length: pool full
+    with pytest.raises(ssa.SSAError):
+        pool.add(cu2, 2, 64, counts2, tiles2)
+    cu3, counts3, tiles3 = _random_pass(rng, 2, 64, 3, [100])  # wrong threshold count
+    with pytest.raises(ssa.SSAError):
+        pool.add(cu3, 2, 64, counts3, tiles3)
+    after = pool.groups
+    assert list(after) == list(before)
+    for k in before:
+        np.testing.assert_array_equal(after[k][0], before[k][0])
+        assert after[k][1] == before[k][1]

@@ -126,3 +126,94 @@ def test_resolve_priority_and_errors():
     assert oc.resolve_threshold(oc.ThresholdSpec(raw_log2=0.5), 10)[0] == oc.ERR_THRESHOLD_RANGE
     st, lam, t = oc.resolve_threshold(oc.ThresholdSpec(lam=0.0), 10)
     assert (st, lam, t) == (oc.OK, 0.0, -INF)
+
+
+# ---- linear-space fit and pooled calibration -------------------------------------
+def test_linear_fit_recovers_exact_curve():
+    a, b, seq_k = 7.93, 8.61, 75600
+    s = np.linspace(0.35, 0.85, 12)
+    f = oc.fit_exponential_linear(a * np.exp(b * s) / seq_k, s, seq_k)
+    assert f.a == pytest.approx(a, rel=1e-12)
+    assert f.b == pytest.approx(b, rel=1e-12)
+    assert (f.s_min, f.s_max, f.n_used) == (pytest.approx(0.35), pytest.approx(0.85), 12)
+
+
+def _noisy(seed, n=14, a=5e-3, b=25.0, sigma=0.3):
+    rng = np.random.default_rng(seed)
+    s = np.sort(rng.uniform(0.3, 0.9, n))
+    y = a * np.exp(b * s) * np.exp(rng.normal(0, sigma, n))
+    return s, y
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_linear_fit_is_a_stationary_point_of_the_squared_error(seed):
+    s, y = _noisy(seed)
+    f = oc.fit_exponential_linear(y / 1000.0, s, 1000.0)
+    e = np.exp(f.b * s)
+    r = f.a * e - y
+    # dF/da = 2 sum r e, dF/db = 2 sum r a s e, relative to the size of the terms
+    assert abs(np.sum(r * e)) <= 1e-9 * np.sum(np.abs(y * e))
+    assert abs(np.sum(r * f.a * s * e)) <= 1e-9 * np.sum(np.abs(y * f.a * s * e))
+    # and no nearby point does better
+    F = np.sum(r * r)
+    for da, db in ((1e-4, 0), (-1e-4, 0), (0, 1e-4), (0, -1e-4)):
+        assert np.sum(((f.a * (1 + da)) * np.exp((f.b + db) * s) - y) ** 2) >= F
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_linear_fit_matches_scipy_curve_fit(seed):
+    from scipy.optimize import curve_fit
+    s, y = _noisy(seed)
+    f = oc.fit_exponential_linear(y / 1000.0, s, 1000.0)
+    lf = oc.fit_exponential_logspace(y / 1000.0, s, 1000.0)
+    p, _ = curve_fit(lambda x, A, B: A * np.exp(B * x), s, y, p0=(lf.a, lf.b), maxfev=50000,
+                     xtol=1e-15, ftol=1e-15, gtol=1e-15)
+    assert f.a == pytest.approx(p[0], rel=1e-6)
+    assert f.b == pytest.approx(p[1], rel=1e-6)
+    # the two fits minimise different errors: on noisy data they differ
+    assert abs(f.b - lf.b) > 1e-6
+
+
+def test_linear_fit_degenerate():
+    with pytest.raises(ValueError):
+        oc.fit_exponential_linear([1e-3, 1e-2], [0.5, 0.5], 100.0)
+    with pytest.raises(ValueError):
+        oc.fit_exponential_linear([1e-3, 1e-2, 1e-1], [0.0, 0.5, 1.0], 100.0)
+
+
+def test_pool_equals_one_pass_over_the_union(tiny):
+    # Two calibration passes (a 2-sequence batch and a 1-sequence batch of
+    # the same key length, plus one of another length) pooled by key length
+    # give the same sparsities as one pass over all sequences together.
+    cfg, x, cu = tiny
+    S = int(cu[1])
+    lams = np.geomspace(1e-4, 0.5, 6)
+    ts = np.log2(lams)
+    q, k, v = x["q"], x["k"], x["v"]
+    half = S // 2
+    cat = lambda parts: np.concatenate(parts, axis=0)
+    # pass A: sequences [0, half) and [half, S); pass B: [0, half) again and [0, 3*half/2)
+    qa, ka, va = q, k, v
+    cua = [0, half, S]
+    qb_, kb_, vb_ = cat([q[:half], q[:3 * half // 2]]), cat([k[:half], k[:3 * half // 2]]), cat([v[:half], v[:3 * half // 2]])
+    cub = [0, half, half + 3 * half // 2]
+    A = osk.calibration_counts(qa, ka, va, cua, ts, cfg.block)
+    B = osk.calibration_counts(qb_, kb_, vb_, cub, ts, cfg.block)
+    pool = oc.CalibPool(len(lams))
+    pool.add(A["counts"], A["tiles"], cua, cfg.num_heads, cfg.block)
+    pool.add(B["counts"], B["tiles"], cub, cfg.num_heads, cfg.block)
+    assert list(pool.groups) == [half, 3 * half // 2]
+    # the union as one varlen pass
+    qu = cat([q[:half], q[half:S], q[:half], q[:3 * half // 2]])
+    ku = cat([k[:half], k[half:S], k[:half], k[:3 * half // 2]])
+    vu = cat([v[:half], v[half:S], v[:half], v[:3 * half // 2]])
+    cuu = [0, half, S, S + half, S + half + 3 * half // 2]
+    U = osk.calibration_counts(qu, ku, vu, cuu, ts, cfg.block)
+    wgs = U["wg"]
+    for key, seqs in ((half, (0, 1, 2)), (3 * half // 2, (3,))):
+        rows = [n for n, (b, h, i) in enumerate(wgs) if b in seqs]
+        skipped, visited = pool.groups[key]
+        np.testing.assert_array_equal(skipped, U["counts"][rows].sum(0))
+        assert visited == U["tiles"][rows].sum()
+    lam_p, sp_p, sk_p = pool.points(lams)
+    assert lam_p.size == 2 * len(lams) and set(sk_p) == {half, 3 * half // 2}
