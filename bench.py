@@ -220,6 +220,20 @@ def main() -> int:
                       "speedup_vs_dense": round(dense_ms / ms_l, 3)})
         log(f"{tag}: lambda {lam:.4g} sparsity {sp_l:.4f} {ms_l:.2f} ms")
 
+    # causal (prefill) form of the same shape: dense and calibrated lambda
+    causal_fwd = lambda lam: (lambda: ssa.attn_fwd(dx["q"], dx["k"], dx["v"], cu, lam, block=blk, out=o, causal=True))
+    ssa.attn_fwd(dx["q"], dx["k"], dx["v"], cu, lam07, block=blk, out=o, skipped=skipped, total=total, causal=True)
+    torch.cuda.synchronize()
+    c_sp = float(skipped.sum()) / float(total.sum())
+    c_dense_ms = time_launches(causal_fwd(0.0), 1, max(2, args.steps // 2))
+    c_ms = time_launches(causal_fwd(lam07), 1, max(2, args.steps // 2))
+    c_flops = 4.0 * H * D * S * (S + 1) / 2  # exact causal (query, key) pairs
+    causal = {"achieved_tile_sparsity": round(c_sp, 4), "dense_ms": round(c_dense_ms, 3), "ms": round(c_ms, 3),
+              "speedup_vs_dense": round(c_dense_ms / c_ms, 3),
+              "dense_tflops": round(c_flops / (c_dense_ms * 1e-3) / 1e12, 2),
+              "tflops_dense_equiv": round(c_flops / (c_ms * 1e-3) / 1e12, 2)}
+    log(f"causal: dense {c_dense_ms:.2f} ms, lambda {lam07:.4g} -> {c_ms:.2f} ms (sparsity {c_sp:.4f})")
+
     dense_flops = cfg.dense_flops()
     exec_flops = dense_flops / 2 * (2 - s_ach)
     value = dense_flops / (sparse_ms * 1e-3) / 1e12
@@ -247,6 +261,7 @@ def main() -> int:
         "executed_tflops": round(exec_tf, 2),
         "sweep": sweep,
         "gating": gating,
+        "causal": causal,
         "calibration": {"pass_ms": round(calib_ms, 3), "fit_resolve_host_ms": round(host_ms, 3),
                         "a": fit.a, "b": fit.b, "s_min": fit.s_min, "s_max": fit.s_max,
                         "n_used": fit.n_used, "resolved": resolved,

@@ -59,10 +59,12 @@ typedef void* ssa_stream_t; /* hipStream_t */
 
 /* ---- problem description ----------------------------------------------- */
 /* Self-attention over B packed sequences: q, k and v share cu_seqlens
- * (S_q = S_k per sequence). Non-causal only ([PR1166] "Usage": is_causal
- * False). The tile size block = Br = Bc is part of the method's definition,
- * because skip decisions are taken per Br x Bc tile ([PR1166] "Usage":
- * br = bc = 128). */
+ * (S_q = S_k per sequence). Diffusion self-attention is non-causal
+ * ([PR1166] "Usage": is_causal False); causal = 1 selects the prefill form
+ * (query i attends keys 0..i of its sequence; [PR1166] "Usage" and [TRTLLM]
+ * "Use Cases" carry the LLM prefill threshold key). The tile size
+ * block = Br = Bc is part of the method's definition, because skip decisions
+ * are taken per Br x Bc tile ([PR1166] "Usage": br = bc = 128). */
 typedef struct ssa_problem {
   int32_t batch;             /* B >= 1 sequences                                  */
   int32_t num_heads;         /* H in [1, 512]                                     */
@@ -74,6 +76,7 @@ typedef struct ssa_problem {
   int64_t stride_token;      /* elements between tokens, same for q, k, v, o       */
   int64_t stride_head;       /* elements between heads, same for q, k, v, o        */
   double sm_scale;           /* softmax scale; 0 selects 1 / sqrt(D)               */
+  int32_t causal;            /* 0 = non-causal, 1 = causal (keys 0..i for query i) */
 } ssa_problem;
 
 /* ---- thresholds for the forward ---------------------------------------- */
@@ -107,7 +110,8 @@ typedef struct ssa_thresholds {
  * skipped when d < log2(lambda): its V is not loaded, no exponential and no
  * P.V is computed, and the running statistics are left unchanged. Kept tiles
  * update the online softmax as in FlashAttention. The first tile is never
- * skipped. Scores are accumulated in fp32 from bf16 inputs, P is rounded to
+ * skipped. With causal = 1, Q-block i visits tiles 0..i only; keys after a
+ * query are excluded from its scores, row maxima and softmax. Scores are accumulated in fp32 from bf16 inputs, P is rounded to
  * bf16 for the P.V product, O is rounded to bf16.
  *
  *  q, k, v    device, bf16 [T, H, D] (see conventions)
@@ -115,6 +119,7 @@ typedef struct ssa_thresholds {
  *  th         host, thresholds (see above)
  *  skipped_bh device uint64 [B * H] or NULL: skipped KV tiles per (b, h)
  *  total_bh   device uint64 [B * H] or NULL: visited KV tiles per (b, h)
+ *             (nQ^2 non-causal, nQ (nQ + 1) / 2 causal)
  *             (both are overwritten, not accumulated: the library zeroes them)
  *  tile_mask  device uint8 [B, H, nq_max, nk_max] or NULL (debug): 0 = tile
  *             kept, 1 = skipped, 2 = no such tile; dims from ssa_tile_mask_dims.

@@ -62,13 +62,17 @@ def _head(x: np.ndarray, s0: int, s1: int, h: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # The textbook definition (dense attention).
 # ---------------------------------------------------------------------------
-def attention_exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float) -> np.ndarray:
+def attention_exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float,
+                    causal: bool = False) -> np.ndarray:
     """softmax(q k^T * sm_scale) v for one head, q [R,D], k/v [S,D], fp64.
 
-    The exact result that dense mode (lambda = 0) must reproduce up to
-    rounding. Pinned by torch's CPU scaled_dot_product_attention in fp64.
+    causal: query r attends keys 0..r only (R == S). The exact result that
+    dense mode (lambda = 0) must reproduce up to rounding. Pinned by torch's
+    CPU scaled_dot_product_attention in fp64 (is_causal for the causal form).
     """
     z = (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T) * sm_scale
+    if causal:
+        z = np.where(np.tril(np.ones(z.shape, dtype=bool)), z, -np.inf)
     z -= z.max(axis=1, keepdims=True)
     p = np.exp(z)
     p /= p.sum(axis=1, keepdims=True)
@@ -78,9 +82,28 @@ def attention_exact(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float
 # ---------------------------------------------------------------------------
 # Sequential form: the tile loop, one Q-block at a time.
 # ---------------------------------------------------------------------------
+def _causal_limit(S: int, block: int, causal_row0: Optional[int], R: int) -> Tuple[int, int]:
+    """(number of KV tiles visited, key columns visible to the block)."""
+    if causal_row0 is None:
+        return n_tiles(S, block), S
+    last = causal_row0 + R - 1            # position of the block's last query
+    nk = last // block + 1
+    return nk, min(S, nk * block)
+
+
+def _causal_mask(s: np.ndarray, causal_row0: Optional[int], col0: int) -> np.ndarray:
+    """Scores with keys after each row's query set to -inf (causal only)."""
+    if causal_row0 is None:
+        return s
+    rows = causal_row0 + np.arange(s.shape[0])[:, None]
+    cols = col0 + np.arange(s.shape[1])[None, :]
+    return np.where(cols <= rows, s, -np.inf)
+
+
 def skip_softmax_qblock(qb: np.ndarray, k: np.ndarray, v: np.ndarray, t: float, block: int,
                         sm_scale: float, forced_skip: Optional[np.ndarray] = None,
-                        calib_ts: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                        calib_ts: Optional[np.ndarray] = None,
+                        causal_row0: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Run the skip-softmax tile loop for one Q-block of one head.
 
     qb: [R, D] valid query rows of the block; k, v: [S, D] the head's keys/values.
@@ -88,6 +111,9 @@ def skip_softmax_qblock(qb: np.ndarray, k: np.ndarray, v: np.ndarray, t: float, 
     bool array that replaces the decisions (used to compare outputs under the
     GPU's own decisions). calib_ts: optional [N] log2 thresholds; when given,
     the loop never skips and counts, per threshold, the tiles with d < t_k.
+    causal_row0: position of the block's first query for causal attention
+    (query at position p sees keys 0..p; only tiles up to the one holding
+    the block's last query are visited); None = non-causal.
 
     Returns dict(o [R,D], d [nK], skip [nK] bool, counts [N] (calibration)).
     Pinned by: the textbook definition at lambda=0, the fast form on small
@@ -99,7 +125,7 @@ def skip_softmax_qblock(qb: np.ndarray, k: np.ndarray, v: np.ndarray, t: float, 
     v = np.asarray(v, np.float64)
     R, D = qb.shape
     S = k.shape[0]
-    nk = n_tiles(S, block)
+    nk, _ = _causal_limit(S, block, causal_row0, R)
     c = sm_scale * LOG2E
 
     m = np.full(R, -np.inf)        # running max (log2 units), before each tile
@@ -112,6 +138,7 @@ def skip_softmax_qblock(qb: np.ndarray, k: np.ndarray, v: np.ndarray, t: float, 
     for j in range(nk):
         j0, j1 = j * block, min(S, (j + 1) * block)
         s = (qb @ k[j0:j1].T) * c                 # scores of tile j, log2 units
+        s = _causal_mask(s, causal_row0, j0)
         rowmax = s.max(axis=1)
         with np.errstate(invalid="ignore"):
             d = float(np.max(rowmax - m))         # m = -inf gives +inf
@@ -138,17 +165,20 @@ def skip_softmax_qblock(qb: np.ndarray, k: np.ndarray, v: np.ndarray, t: float, 
 # ---------------------------------------------------------------------------
 # Fast form (valid for lambda <= 1): decisions from the dense prefix maximum.
 # ---------------------------------------------------------------------------
-def tile_stats_fast(qb: np.ndarray, k: np.ndarray, block: int, sm_scale: float
-                    ) -> Tuple[np.ndarray, np.ndarray]:
+def tile_stats_fast(qb: np.ndarray, k: np.ndarray, block: int, sm_scale: float,
+                    causal_row0: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
     """d_j for every KV tile of one Q-block, from the dense prefix maximum.
 
     For lambda <= 1 a skipped tile has rowmax_r < m_r in every row, so the
     running maximum before tile j always equals the prefix maximum over
     tiles 0..j-1 whatever was skipped; d_j therefore does not depend on the
-    threshold. Returns (d [nK], scores [R, S] in log2 units).
+    threshold. Returns (d [nK], scores [R, visible keys] in log2 units).
     Pinned by equality with the sequential form (tests).
     """
-    s = (np.asarray(qb, np.float64) @ np.asarray(k, np.float64).T) * (sm_scale * LOG2E)
+    qb = np.asarray(qb, np.float64)
+    _, kv_end = _causal_limit(k.shape[0], block, causal_row0, qb.shape[0])
+    s = (qb @ np.asarray(k, np.float64)[:kv_end].T) * (sm_scale * LOG2E)
+    s = _causal_mask(s, causal_row0, 0)
     S = s.shape[1]
     starts = np.arange(0, S, block)
     tile_max = np.maximum.reduceat(s, starts, axis=1)            # [R, nK]
@@ -161,20 +191,20 @@ def tile_stats_fast(qb: np.ndarray, k: np.ndarray, block: int, sm_scale: float
 
 
 def skip_softmax_qblock_fast(qb: np.ndarray, k: np.ndarray, v: np.ndarray, t: float, block: int,
-                             sm_scale: float, forced_skip: Optional[np.ndarray] = None
-                             ) -> Dict[str, np.ndarray]:
+                             sm_scale: float, forced_skip: Optional[np.ndarray] = None,
+                             causal_row0: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Fast form of `skip_softmax_qblock` for t <= 0 (lambda <= 1).
 
     The output is the exact softmax restricted to the kept tiles' keys,
     renormalised: each row's overall maximum lies in a kept tile.
     """
-    d, s = tile_stats_fast(qb, k, block, sm_scale)
+    d, s = tile_stats_fast(qb, k, block, sm_scale, causal_row0)
     skip = (d < t) if forced_skip is None else np.asarray(forced_skip, bool)
     keep_cols = np.repeat(~skip, block)[: s.shape[1]]
     sk = np.where(keep_cols[None, :], s, -np.inf)
     mx = sk.max(axis=1, keepdims=True)
     p = np.exp2(sk - mx)
-    o = (p @ np.asarray(v, np.float64)) / p.sum(axis=1, keepdims=True)
+    o = (p @ np.asarray(v, np.float64)[: s.shape[1]]) / p.sum(axis=1, keepdims=True)
     return {"o": o, "d": d, "skip": skip}
 
 
@@ -197,9 +227,9 @@ def workgroups(cu_seqlens: Sequence[int], num_heads: int, block: int) -> List[Tu
 
 def skip_softmax_forward(q, k, v, cu_seqlens, t_bh, block: int, sm_scale: Optional[float] = None,
                          qblocks: Optional[Iterable[Tuple[int, int, int]]] = None,
-                         forced_mask: Optional[np.ndarray] = None, fast: bool = False
-                         ) -> Dict[str, np.ndarray]:
-    """Skip-softmax forward over a packed varlen batch.
+                         forced_mask: Optional[np.ndarray] = None, fast: bool = False,
+                         causal: bool = False) -> Dict[str, np.ndarray]:
+    """Skip-softmax forward over a packed varlen batch (causal: prefill form).
 
     t_bh: [B, H] log2 thresholds. qblocks: optional subset of (b, h, i) to
     compute (others are left NaN / TILE_NONE). forced_mask: optional
@@ -228,10 +258,11 @@ def skip_softmax_forward(q, k, v, cu_seqlens, t_bh, block: int, sm_scale: Option
             heads_cache[(b, h)] = (_head(q, s0, s1, h), _head(k, s0, s1, h), _head(v, s0, s1, h))
         qh, kh, vh = heads_cache[(b, h)]
         r0, r1 = i * block, min(s1 - s0, (i + 1) * block)
-        nk = n_tiles(s1 - s0, block)
+        nk = i + 1 if causal else n_tiles(s1 - s0, block)
         forced = None if forced_mask is None else forced_mask[b, h, i, :nk] == TILE_SKIPPED
         fn = skip_softmax_qblock_fast if fast else skip_softmax_qblock
-        res = fn(qh[r0:r1], kh, vh, float(t_bh[b, h]), block, scale, forced_skip=forced)
+        res = fn(qh[r0:r1], kh, vh, float(t_bh[b, h]), block, scale, forced_skip=forced,
+                 causal_row0=r0 if causal else None)
         o[s0 + r0:s0 + r1, h, :] = res["o"]
         mask[b, h, i, :nk] = np.where(res["skip"], TILE_SKIPPED, TILE_KEPT)
         dd[b, h, i, :nk] = res["d"]
@@ -242,8 +273,8 @@ def skip_softmax_forward(q, k, v, cu_seqlens, t_bh, block: int, sm_scale: Option
 
 def calibration_counts(q, k, v, cu_seqlens, log2_ts: Sequence[float], block: int,
                        sm_scale: Optional[float] = None,
-                       qblocks: Optional[Iterable[Tuple[int, int, int]]] = None
-                       ) -> Dict[str, np.ndarray]:
+                       qblocks: Optional[Iterable[Tuple[int, int, int]]] = None,
+                       causal: bool = False) -> Dict[str, np.ndarray]:
     """The calibration pass: dense attention plus, per Q-block (work-group)
     and per threshold t_k, the number of tiles that would be skipped (d < t_k).
 
@@ -271,7 +302,8 @@ def calibration_counts(q, k, v, cu_seqlens, log2_ts: Sequence[float], block: int
             cache[(b, h)] = (_head(q, s0, s1, h), _head(k, s0, s1, h), _head(v, s0, s1, h))
         qh, kh, vh = cache[(b, h)]
         r0, r1 = i * block, min(s1 - s0, (i + 1) * block)
-        res = skip_softmax_qblock(qh[r0:r1], kh, vh, float("-inf"), block, scale, calib_ts=ts)
+        res = skip_softmax_qblock(qh[r0:r1], kh, vh, float("-inf"), block, scale, calib_ts=ts,
+                                  causal_row0=r0 if causal else None)
         n = index[(b, h, i)]
         counts[n] = res["counts"]
         tiles[n] = len(res["d"])

@@ -64,6 +64,7 @@ class Problem(ctypes.Structure):
         ("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("block", ctypes.c_int32), ("cu_seqlens", ctypes.POINTER(ctypes.c_int32)),
         ("stride_token", ctypes.c_int64), ("stride_head", ctypes.c_int64), ("sm_scale", ctypes.c_double),
+        ("causal", ctypes.c_int32),
     ]
 
 
@@ -149,13 +150,15 @@ def _check(status: int, where: str) -> int:
 
 
 # ---- problem marshalling -----------------------------------------------------
-def make_problem(q, cu_seqlens, block: int, sm_scale: float = 0.0) -> Tuple[Problem, np.ndarray]:
+def make_problem(q, cu_seqlens, block: int, sm_scale: float = 0.0, causal: bool = False
+                 ) -> Tuple[Problem, np.ndarray]:
     """ssa_problem for a [T, H, D] tensor; returns (struct, cu array kept alive)."""
     cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
     T, H, D = q.shape
     prob = Problem(batch=len(cu) - 1, num_heads=H, head_dim=D, block=block,
                    cu_seqlens=cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                   stride_token=q.stride(0), stride_head=q.stride(1), sm_scale=float(sm_scale))
+                   stride_token=q.stride(0), stride_head=q.stride(1), sm_scale=float(sm_scale),
+                   causal=1 if causal else 0)
     return prob, cu
 
 
@@ -196,7 +199,7 @@ def calib_num_workgroups(prob: Problem) -> int:
 # ---- entry points -------------------------------------------------------------
 def attn_fwd(q, k, v, cu_seqlens, threshold: Union[float, Sequence[float]], kind: str = "lambda",
              block: int = 128, sm_scale: float = 0.0, out=None, skipped=None, total=None,
-             tile_mask=None, stream=None):
+             tile_mask=None, stream=None, causal: bool = False):
     """ssa_attn_fwd on torch tensors; returns `out` (allocated when None).
 
     threshold: one value for every head, or H values (per head); `kind` is
@@ -208,7 +211,7 @@ def attn_fwd(q, k, v, cu_seqlens, threshold: Union[float, Sequence[float]], kind
     if out is None:
         out = torch.empty_like(q)
     _check_qkv(q, k, v, out)
-    prob, cu = make_problem(q, cu_seqlens, block, sm_scale)
+    prob, cu = make_problem(q, cu_seqlens, block, sm_scale, causal)
     vals = np.ascontiguousarray(np.atleast_1d(np.asarray(threshold, dtype=np.float64)))
     th = Thresholds(kind=_KINDS[kind], count=vals.size, values=vals.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     st = load_library().ssa_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(th),
@@ -218,13 +221,13 @@ def attn_fwd(q, k, v, cu_seqlens, threshold: Union[float, Sequence[float]], kind
 
 
 def attn_calibrate(q, k, v, cu_seqlens, lambdas: Sequence[float], block: int = 128, sm_scale: float = 0.0,
-                   out=None, counts=None, tiles=None, stream=None):
+                   out=None, counts=None, tiles=None, stream=None, causal: bool = False):
     """ssa_attn_calibrate; returns (out, counts [num_wg, n] int32, tiles [num_wg] int32) on the device."""
     import torch
     if out is None:
         out = torch.empty_like(q)
     _check_qkv(q, k, v, out)
-    prob, cu = make_problem(q, cu_seqlens, block, sm_scale)
+    prob, cu = make_problem(q, cu_seqlens, block, sm_scale, causal)
     lam = np.ascontiguousarray(np.asarray(lambdas, dtype=np.float64))
     nwg = calib_num_workgroups(prob)
     if counts is None:

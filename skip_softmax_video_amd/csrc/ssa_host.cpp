@@ -43,6 +43,7 @@ int validate_problem(const ssa_problem* p) {
   if (p->stride_token < p->head_dim) return SSA_ERR_INVALID_ARG;
   if (p->num_heads > 1 && p->stride_head < p->head_dim) return SSA_ERR_INVALID_ARG;
   if (!(p->sm_scale >= 0.0) || !isfinite(p->sm_scale)) return SSA_ERR_INVALID_ARG;
+  if (p->causal != 0 && p->causal != 1) return SSA_ERR_INVALID_ARG;
   return SSA_OK;
 }
 
@@ -134,6 +135,7 @@ ssa::LaunchParams base_params(const ssa_problem* p, const void* q, const void* k
   lp.stride_head = p->stride_head;
   lp.scale_log2 = (float)(effective_scale(p) * 1.4426950408889634);  // * log2(e)
   lp.num_heads = p->num_heads;
+  lp.causal = p->causal;
   return lp;
 }
 

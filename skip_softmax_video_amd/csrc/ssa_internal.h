@@ -23,6 +23,7 @@ struct LaunchParams {
   int64_t stride_head; // elements
   float scale_log2;    // sm_scale * log2(e)
   int32_t num_heads;
+  int32_t causal;                            // 1: Q-block i visits KV tiles 0..i, keys after the query masked
   int32_t nseq;                              // sequences in this launch
   int32_t total_wg;                          // work-groups in this launch
   int32_t seq_abs0;                          // batch index of the first sequence

@@ -204,8 +204,10 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
   const int nQ = (S + BLK - 1) / BLK;
   const int rem = L - p.wg_start[b];
   const int h = rem / nQ;
-  const int qb = rem - h * nQ;
-  const int nK = nQ;
+  // causal: the longest Q-blocks (most KV tiles) are dispatched first
+  const int qb = p.causal ? nQ - 1 - (rem - h * nQ) : rem - h * nQ;
+  const int nK = p.causal ? qb + 1 : nQ;
+  const int row = p.wg_start[b] + h * nQ + qb;  // (sequence, head, Q-block) index of count-table rows
   const int H = p.num_heads;
   const int64_t head_off = (int64_t)tok0 * p.stride_tok + (int64_t)h * p.stride_head;
   const uint16_t* kbase = p.k + head_off;
@@ -272,13 +274,15 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
         sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s & 1][kb], qf[s], sc[kb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (nvalid < BLK) {
+    // keys past the sequence end; causal: keys after this lane's query (diagonal tile)
+    const int kmax = (p.causal && j == qb) ? min(nvalid, wave * 32 + l32 + 1) : nvalid;
+    if (p.causal ? j == qb : nvalid < BLK) {
 #pragma unroll
       for (int kb = 0; kb < SH::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key >= nvalid) sc[kb][r] = -INFINITY;
+          if (key >= kmax) sc[kb][r] = -INFINITY;
         }
     }
 
@@ -384,8 +388,8 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
       }
   }
   if constexpr (CALIB) {
-    if (wave == 0 && lane < ncal) p.counts[(p.wg_abs0 + L) * ncal + lane] = ncount;
-    if (tid == 0) p.tiles[p.wg_abs0 + L] = nK;
+    if (wave == 0 && lane < ncal) p.counts[(p.wg_abs0 + row) * ncal + lane] = ncount;
+    if (tid == 0) p.tiles[p.wg_abs0 + row] = nK;
   } else {
     if (tid == 0) {
       const int64_t bh = (int64_t)(p.seq_abs0 + b) * H + h;

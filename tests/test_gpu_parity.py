@@ -41,18 +41,18 @@ def _f64(x):
     return {n: to_f64(x[n]) for n in ("q", "k", "v")}
 
 
-def _full_parity(cfg, threshold, kind="lambda", block=None):
+def _full_parity(cfg, threshold, kind="lambda", block=None, causal=False):
     block = block or cfg.block
     x, xd, cu = _inputs(cfg)
     xf = _f64(x)
     H = cfg.num_heads
-    log(f"[{cfg.name}] D={cfg.head_dim} block={block} threshold={threshold} kind={kind}")
-    o, sk, tot, mask = gpu_forward(xd, cu, threshold, kind, block)
+    log(f"[{cfg.name}] D={cfg.head_dim} block={block} threshold={threshold} kind={kind} causal={causal}")
+    o, sk, tot, mask = gpu_forward(xd, cu, threshold, kind, block, causal=causal)
     t = t_matrix(cu, H, threshold, kind)
-    ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, block)
+    ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, block, causal=causal)
     wgs = osk.workgroups(cu, H, block)
     band, mism = compare_masks(mask, ref, t, wgs)
-    forced = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, block, forced_mask=mask)
+    forced = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, block, forced_mask=mask, causal=causal)
     mx, mean = compare_outputs(o, forced["o"])
     np.testing.assert_array_equal(sk, (mask == osk.TILE_SKIPPED).sum(axis=(2, 3)))
     np.testing.assert_array_equal(tot, ref["total"])
@@ -172,7 +172,7 @@ def test_untouched_memory_outside_valid_rows():
     compare_outputs(o.float().cpu().numpy(), ref["o"])
 
 
-def _sampled_parity(cfg, lams, heads, per_head):
+def _sampled_parity(cfg, lams, heads, per_head, causal=False):
     """Full-size launch; outputs and skip bits checked on sampled Q-blocks
     (first, last/partial and random ones) that the oracle computes one by one."""
     x, xd, cu = _inputs(cfg)
@@ -181,10 +181,11 @@ def _sampled_parity(cfg, lams, heads, per_head):
     qbs = sample_qblocks(cu, H, blk, heads, per_head, seed=cfg.seed)
     fracs = []
     for lam in lams:
-        log(f"[{cfg.name}] lambda={lam}: GPU forward (full launch)")
-        o, sk, tot, mask = gpu_forward(xd, cu, lam, "lambda", blk)
+        log(f"[{cfg.name}] lambda={lam} causal={causal}: GPU forward (full launch)")
+        o, sk, tot, mask = gpu_forward(xd, cu, lam, "lambda", blk, causal=causal)
         t = t_matrix(cu, H, lam, "lambda")
-        want_tot = np.array([[osk.n_tiles(int(cu[b + 1] - cu[b]), blk) ** 2] * H for b in range(len(cu) - 1)])
+        nqs = [osk.n_tiles(int(cu[b + 1] - cu[b]), blk) for b in range(len(cu) - 1)]
+        want_tot = np.array([[n * (n + 1) // 2 if causal else n * n] * H for n in nqs])
         np.testing.assert_array_equal(tot, want_tot)
         np.testing.assert_array_equal(sk, (mask == osk.TILE_SKIPPED).sum(axis=(2, 3)))
         log(f"  oracle on {len(qbs)} sampled Q-blocks")
@@ -199,8 +200,8 @@ def _sampled_parity(cfg, lams, heads, per_head):
             kh, vh = cache[(b, h)]
             r0, r1 = i * blk, min(s1 - s0, (i + 1) * blk)
             qh = to_f64(x["q"][s0 + r0:s0 + r1, h])
-            nk = osk.n_tiles(s1 - s0, blk)
-            d, _ = osk.tile_stats_fast(qh, kh, blk, scale)
+            nk = i + 1 if causal else osk.n_tiles(s1 - s0, blk)
+            d, _ = osk.tile_stats_fast(qh, kh, blk, scale, causal_row0=r0 if causal else None)
             ref_skip = d < t[b, h]
             gpu_skip = mask[b, h, i, :nk] == osk.TILE_SKIPPED
             assert np.all(mask[b, h, i, nk:] == osk.TILE_NONE)
@@ -209,7 +210,8 @@ def _sampled_parity(cfg, lams, heads, per_head):
             assert not np.any(hard), f"skip mismatch at {(b, h, i)} tiles {np.nonzero(hard)[0][:8]}"
             band += int(near.sum())
             mism += int(((gpu_skip != ref_skip) & near).sum())
-            ref = osk.skip_softmax_qblock(qh, kh, vh, t[b, h], blk, scale, forced_skip=gpu_skip)
+            ref = osk.skip_softmax_qblock(qh, kh, vh, t[b, h], blk, scale, forced_skip=gpu_skip,
+                                          causal_row0=r0 if causal else None)
             diff = np.abs(o[s0 + r0:s0 + r1, h] - ref["o"])
             worst_max = max(worst_max, float(diff.max()))
             sum_abs += float(diff.sum())
@@ -305,3 +307,48 @@ def test_pooled_calibration_multi_sample_multi_shape():
         r = ofit(lam_r, sp_r, sk_r)
         log(f"  {space}: a={g.a:.5g} b={g.b:.5g} (oracle a={r.a:.5g} b={r.b:.5g}) points {g.n_used}")
         assert g.b == pytest.approx(r.b, rel=1e-3) and g.a == pytest.approx(r.a, rel=1e-3)
+
+
+# ---- causal (prefill) form ---------------------------------------------------------
+@pytest.mark.parametrize("lam", [0.0, 1e-2, 1.0])
+def test_causal_tiny_parity(lam):
+    sk, tot, mask, _ = _full_parity(CONFIGS["tiny"], lam, causal=True)
+    nq = 1024 // 64
+    assert np.all(tot == nq * (nq + 1) // 2)
+    assert (sk.sum() == 0) == (lam == 0.0)
+
+
+@pytest.mark.parametrize("lam", [0.0, 1e-2])
+def test_causal_ragged_d128_parity(lam):
+    _full_parity(RAGGED, lam, causal=True)
+
+
+def test_causal_calibration_counts():
+    import torch
+    import skip_softmax_video_amd as ssa
+    cfg = RAGGED
+    x, xd, cu = _inputs(cfg)
+    xf = _f64(x)
+    lams = np.geomspace(1e-5, 0.7, 8)
+    o_cal, counts, tiles = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, lams, block=cfg.block, causal=True)
+    torch.cuda.synchronize()
+    counts, tiles = counts.cpu().numpy(), tiles.cpu().numpy()
+    wgs = osk.workgroups(cu, cfg.num_heads, cfg.block)
+    np.testing.assert_array_equal(tiles, [i + 1 for (_, _, i) in wgs])
+    o0, _, _, _ = gpu_forward(xd, cu, 0.0, "lambda", cfg.block, mask=False, causal=True)
+    np.testing.assert_array_equal(o_cal.float().cpu().numpy(), o0)
+    ts = np.log2(lams)
+    ref = osk.calibration_counts(xf["q"], xf["k"], xf["v"], cu, ts, cfg.block, causal=True)
+    d = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, -math.inf, cfg.block, fast=True, causal=True)["d"]
+    for kk, lam in enumerate(lams):
+        _, _, _, mask = gpu_forward(xd, cu, lam, "lambda", cfg.block, causal=True)
+        per_wg = np.array([(mask[b, h, i] == osk.TILE_SKIPPED).sum() for (b, h, i) in wgs])
+        np.testing.assert_array_equal(counts[:, kk], per_wg)
+        with np.errstate(invalid="ignore"):
+            band = np.array([np.sum(np.abs(d[b, h, i] - ts[kk]) <= 1e-3) for (b, h, i) in wgs])
+        assert np.all(np.abs(counts[:, kk] - ref["counts"][:, kk]) <= band)
+
+
+def test_causal_headline_sampled_parity():
+    fr = _sampled_parity(CONFIGS["headline"], [0.0, 8e-3], heads=[0, 39], per_head=3, causal=True)
+    assert fr[0] == 0.0 and fr[1] > 0.1

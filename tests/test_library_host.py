@@ -126,6 +126,8 @@ FAKE = 1 << 20  # aligned, never dereferenced: validation fails first
     (dict(cu=[3, 10]), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
     (dict(stride_token=100), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
     (dict(sm_scale=-1.0), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(causal=2), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(causal=-1), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
     (dict(), (0, [1.5]), ssa.SSA_ERR_THRESHOLD_RANGE),
     (dict(), (0, [float("nan")]), ssa.SSA_ERR_THRESHOLD_RANGE),
     (dict(), (1, [0.25]), ssa.SSA_ERR_THRESHOLD_RANGE),            # raw log2 > 0
