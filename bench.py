@@ -29,6 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA, published
 TARGET_SPARSITY = 0.7
 CALIB_LAMBDAS_N = 16
 KERNEL_SOURCE = os.path.join(ROOT, "skip_softmax_video_amd", "csrc", "ssa_kernel.hip")
@@ -234,11 +235,36 @@ def main() -> int:
               "tflops_dense_equiv": round(c_flops / (c_ms * 1e-3) / 1e12, 2)}
     log(f"causal: dense {c_dense_ms:.2f} ms, lambda {lam07:.4g} -> {c_ms:.2f} ms (sparsity {c_sp:.4f})")
 
+    # FP8 (e4m3) variant of the same inputs: per-tensor quantized on the host
+    from synth import make_fp8_inputs
+    log("quantizing the headline sample to e4m3")
+    f8 = make_fp8_inputs(x)
+    d8 = {n: torch.from_numpy(f8[n + "8"]).cuda() for n in ("q", "k", "v")}
+    sc8 = (f8["scale_q"], f8["scale_k"], f8["scale_v"])
+    del f8
+    fp8_fwd = lambda lam: (lambda: ssa.attn_fwd(d8["q"], d8["k"], d8["v"], cu, lam, block=blk, out=o, scales=sc8))
+    ssa.attn_fwd(d8["q"], d8["k"], d8["v"], cu, lam07, block=blk, out=o, skipped=skipped, total=total, scales=sc8)
+    torch.cuda.synchronize()
+    f_sp = float(skipped.sum()) / float(total.sum())
+    f_dense_ms = time_launches(fp8_fwd(0.0), args.warmup, args.steps)
+    f_ms = time_launches(fp8_fwd(lam07), args.warmup, args.steps)
+    f_exec = cfg.dense_flops() / 2 * (2 - f_sp)
+    fp8 = {"achieved_tile_sparsity": round(f_sp, 4), "dense_ms": round(f_dense_ms, 3), "ms": round(f_ms, 3),
+           "speedup_vs_dense": round(f_dense_ms / f_ms, 3), "speedup_vs_bf16_same_lambda": None,
+           "dense_tflops": round(cfg.dense_flops() / (f_dense_ms * 1e-3) / 1e12, 2),
+           "tflops_dense_equiv": round(cfg.dense_flops() / (f_ms * 1e-3) / 1e12, 2),
+           "executed_tflops": round(f_exec / (f_ms * 1e-3) / 1e12, 2),
+           "frac_of_fp8_peak": round(f_exec / (f_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+           "scales": [float(v) for v in sc8]}
+    log(f"fp8: dense {f_dense_ms:.2f} ms, lambda {lam07:.4g} -> {f_ms:.2f} ms (sparsity {f_sp:.4f})")
+    del d8
+
     dense_flops = cfg.dense_flops()
     exec_flops = dense_flops / 2 * (2 - s_ach)
     value = dense_flops / (sparse_ms * 1e-3) / 1e12
     dense_tf = dense_flops / (dense_ms * 1e-3) / 1e12
     exec_tf = exec_flops / (sparse_ms * 1e-3) / 1e12
+    fp8["speedup_vs_bf16_same_lambda"] = round(sparse_ms / fp8["ms"], 3)
     result = {
         "metric": "skip-softmax attn TFLOPS (dense-equiv) + speedup vs dense @S=75,600 H=40 D=128",
         "value": round(value, 2),
@@ -262,6 +288,7 @@ def main() -> int:
         "sweep": sweep,
         "gating": gating,
         "causal": causal,
+        "fp8": fp8,
         "calibration": {"pass_ms": round(calib_ms, 3), "fit_resolve_host_ms": round(host_ms, 3),
                         "a": fit.a, "b": fit.b, "s_min": fit.s_min, "s_max": fit.s_max,
                         "n_used": fit.n_used, "resolved": resolved,

@@ -77,7 +77,21 @@ typedef struct ssa_problem {
   int64_t stride_head;       /* elements between heads, same for q, k, v, o        */
   double sm_scale;           /* softmax scale; 0 selects 1 / sqrt(D)               */
   int32_t causal;            /* 0 = non-causal, 1 = causal (keys 0..i for query i) */
+  int32_t dtype;             /* SSA_DTYPE_*: element type of q, k and v (o is bf16) */
+  double scale_q, scale_k, scale_v; /* SSA_DTYPE_FP8_E4M3: dequantization scales,
+                                value = code * scale, each finite and > 0; ignored
+                                for bf16                                           */
 } ssa_problem;
+
+/* Element types of q, k, v. SSA_DTYPE_FP8_E4M3 is the OCP e4m3 ("e4m3fn")
+ * byte format with one scale per tensor: Q K^T and P V run on the fp8
+ * matrix cores, P is rounded to e4m3 (round to nearest even) for P V, the
+ * skip test uses the fp32 scores of the dequantized values, and o is bf16
+ * with the same element strides. Row starts must be 16-byte aligned (strides
+ * multiples of 16 elements). ([TRTLLM] "Use Cases" and [DOCS] list FP8
+ * attention beside BF16.) */
+#define SSA_DTYPE_BF16     0
+#define SSA_DTYPE_FP8_E4M3 1
 
 /* ---- thresholds for the forward ---------------------------------------- */
 /* How the per-(sequence, head) threshold reaches the kernel ([README]

@@ -26,6 +26,9 @@ SSA_ERR_NO_FORMULA = -4
 SSA_ERR_FIT_DEGENERATE = -5
 SSA_ERR_HIP = -6
 
+DTYPE_BF16 = 0
+DTYPE_FP8_E4M3 = 1
+
 THRESH_LAMBDA = 0
 THRESH_LOG2 = 1
 THRESH_SCALE_FACTOR = 2
@@ -64,7 +67,8 @@ class Problem(ctypes.Structure):
         ("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("block", ctypes.c_int32), ("cu_seqlens", ctypes.POINTER(ctypes.c_int32)),
         ("stride_token", ctypes.c_int64), ("stride_head", ctypes.c_int64), ("sm_scale", ctypes.c_double),
-        ("causal", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("scale_q", ctypes.c_double), ("scale_k", ctypes.c_double), ("scale_v", ctypes.c_double),
     ]
 
 
@@ -150,15 +154,24 @@ def _check(status: int, where: str) -> int:
 
 
 # ---- problem marshalling -----------------------------------------------------
-def make_problem(q, cu_seqlens, block: int, sm_scale: float = 0.0, causal: bool = False
-                 ) -> Tuple[Problem, np.ndarray]:
-    """ssa_problem for a [T, H, D] tensor; returns (struct, cu array kept alive)."""
+def _is_fp8(t) -> bool:
+    import torch
+    return t.dtype in (torch.float8_e4m3fn, torch.uint8)
+
+
+def make_problem(q, cu_seqlens, block: int, sm_scale: float = 0.0, causal: bool = False,
+                 scales: Optional[Tuple[float, float, float]] = None) -> Tuple[Problem, np.ndarray]:
+    """ssa_problem for a [T, H, D] tensor (bf16, or e4m3 bytes with `scales` =
+    (scale_q, scale_k, scale_v)); returns (struct, cu array kept alive)."""
     cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
     T, H, D = q.shape
+    fp8 = _is_fp8(q)
+    sq, sk, sv = scales if scales is not None else (1.0, 1.0, 1.0)
     prob = Problem(batch=len(cu) - 1, num_heads=H, head_dim=D, block=block,
                    cu_seqlens=cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                    stride_token=q.stride(0), stride_head=q.stride(1), sm_scale=float(sm_scale),
-                   causal=1 if causal else 0)
+                   causal=1 if causal else 0, dtype=DTYPE_FP8_E4M3 if fp8 else DTYPE_BF16,
+                   scale_q=float(sq), scale_k=float(sk), scale_v=float(sv))
     return prob, cu
 
 
@@ -175,9 +188,11 @@ def _stream(stream) -> Optional[int]:
 
 def _check_qkv(q, k, v, o):
     import torch
+    fp8 = _is_fp8(q)
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3:
-            raise ValueError(f"{name} must be a 3-D bf16 device tensor [T, H, D]")
+        want = torch.bfloat16 if (name == "o" or not fp8) else q.dtype
+        if t.dtype != want or not t.is_cuda or t.dim() != 3:
+            raise ValueError(f"{name} must be a 3-D {want} device tensor [T, H, D]")
         if t.shape != q.shape or t.stride() != q.stride():
             raise ValueError(f"{name} must match q's shape and strides")
 
@@ -199,19 +214,21 @@ def calib_num_workgroups(prob: Problem) -> int:
 # ---- entry points -------------------------------------------------------------
 def attn_fwd(q, k, v, cu_seqlens, threshold: Union[float, Sequence[float]], kind: str = "lambda",
              block: int = 128, sm_scale: float = 0.0, out=None, skipped=None, total=None,
-             tile_mask=None, stream=None, causal: bool = False):
+             tile_mask=None, stream=None, causal: bool = False,
+             scales: Optional[Tuple[float, float, float]] = None):
     """ssa_attn_fwd on torch tensors; returns `out` (allocated when None).
 
     threshold: one value for every head, or H values (per head); `kind` is
     "lambda", "log2" (raw) or "scale_factor" (lambda = sf / S_b).
     skipped/total: optional uint64 device tensors [B*H]; tile_mask: optional
-    uint8 device tensor [B, H, nq, nk].
+    uint8 device tensor [B, H, nq, nk]. q, k, v may be e4m3 (torch.float8_e4m3fn
+    or uint8 bytes) with scales = (scale_q, scale_k, scale_v); out is bf16.
     """
     import torch
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     _check_qkv(q, k, v, out)
-    prob, cu = make_problem(q, cu_seqlens, block, sm_scale, causal)
+    prob, cu = make_problem(q, cu_seqlens, block, sm_scale, causal, scales)
     vals = np.ascontiguousarray(np.atleast_1d(np.asarray(threshold, dtype=np.float64)))
     th = Thresholds(kind=_KINDS[kind], count=vals.size, values=vals.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     st = load_library().ssa_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(th),
@@ -221,13 +238,14 @@ def attn_fwd(q, k, v, cu_seqlens, threshold: Union[float, Sequence[float]], kind
 
 
 def attn_calibrate(q, k, v, cu_seqlens, lambdas: Sequence[float], block: int = 128, sm_scale: float = 0.0,
-                   out=None, counts=None, tiles=None, stream=None, causal: bool = False):
+                   out=None, counts=None, tiles=None, stream=None, causal: bool = False,
+                   scales: Optional[Tuple[float, float, float]] = None):
     """ssa_attn_calibrate; returns (out, counts [num_wg, n] int32, tiles [num_wg] int32) on the device."""
     import torch
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     _check_qkv(q, k, v, out)
-    prob, cu = make_problem(q, cu_seqlens, block, sm_scale, causal)
+    prob, cu = make_problem(q, cu_seqlens, block, sm_scale, causal, scales)
     lam = np.ascontiguousarray(np.asarray(lambdas, dtype=np.float64))
     nwg = calib_num_workgroups(prob)
     if counts is None:

@@ -34,7 +34,8 @@ int validate_problem(const ssa_problem* p) {
     // work-groups of one sequence and tile-mask rows are indexed in int32
     if (ceil_div(s, p->block) * p->num_heads > INT32_MAX / 2) return SSA_ERR_UNSUPPORTED;
     // K/V tiles are fetched through 32-bit buffer offsets from the head's first row
-    if (s > 0 && ((s - 1) * p->stride_token + p->block * p->stride_token + p->head_dim) * 2 > (int64_t)UINT32_MAX)
+    const int64_t esize = p->dtype == SSA_DTYPE_FP8_E4M3 ? 1 : 2;
+    if (s > 0 && ((s - 1) * p->stride_token + p->block * p->stride_token + p->head_dim) * esize > (int64_t)UINT32_MAX)
       return SSA_ERR_UNSUPPORTED;
   }
   // 16-byte aligned rows; distinct tokens (and heads, when H > 1) start at
@@ -44,6 +45,13 @@ int validate_problem(const ssa_problem* p) {
   if (p->num_heads > 1 && p->stride_head < p->head_dim) return SSA_ERR_INVALID_ARG;
   if (!(p->sm_scale >= 0.0) || !isfinite(p->sm_scale)) return SSA_ERR_INVALID_ARG;
   if (p->causal != 0 && p->causal != 1) return SSA_ERR_INVALID_ARG;
+  if (p->dtype != SSA_DTYPE_BF16 && p->dtype != SSA_DTYPE_FP8_E4M3) return SSA_ERR_INVALID_ARG;
+  if (p->dtype == SSA_DTYPE_FP8_E4M3) {
+    // 16-byte aligned e4m3 rows; positive finite dequantization scales
+    if (p->stride_token % 16 != 0 || p->stride_head % 16 != 0) return SSA_ERR_INVALID_ARG;
+    for (double sc : {p->scale_q, p->scale_k, p->scale_v})
+      if (!(sc > 0.0) || !isfinite(sc)) return SSA_ERR_INVALID_ARG;
+  }
   return SSA_OK;
 }
 
@@ -133,9 +141,13 @@ ssa::LaunchParams base_params(const ssa_problem* p, const void* q, const void* k
   lp.o = (uint16_t*)o;
   lp.stride_tok = p->stride_token;
   lp.stride_head = p->stride_head;
-  lp.scale_log2 = (float)(effective_scale(p) * 1.4426950408889634);  // * log2(e)
+  const bool fp8 = p->dtype == SSA_DTYPE_FP8_E4M3;
+  // * log2(e); e4m3 scores also carry the q and k dequantization scales
+  lp.scale_log2 = (float)(effective_scale(p) * 1.4426950408889634 * (fp8 ? p->scale_q * p->scale_k : 1.0));
   lp.num_heads = p->num_heads;
   lp.causal = p->causal;
+  lp.fp8 = fp8 ? 1 : 0;
+  lp.v_scale = fp8 ? (float)p->scale_v : 1.0f;
   return lp;
 }
 

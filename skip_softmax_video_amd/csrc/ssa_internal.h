@@ -24,6 +24,8 @@ struct LaunchParams {
   float scale_log2;    // sm_scale * log2(e)
   int32_t num_heads;
   int32_t causal;                            // 1: Q-block i visits KV tiles 0..i, keys after the query masked
+  int32_t fp8;                               // 1: q, k, v are e4m3 bytes (o stays bf16)
+  float v_scale;                             // fp8: dequantization scale of v (1 for bf16)
   int32_t nseq;                              // sequences in this launch
   int32_t total_wg;                          // work-groups in this launch
   int32_t seq_abs0;                          // batch index of the first sequence

@@ -399,6 +399,319 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
   }
 }
 
+// ===========================================================================
+// FP8 (OCP e4m3) variant: the same tile loop with Q K^T and P V on the
+// fp8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4, unit block scales).
+// Q, K, V are e4m3 with per-tensor dequantization scales; scores are
+// (q8 . k8) * scale_q * scale_k * sm_scale * log2(e) in fp32, so the skip
+// test is the bf16 kernel's test on the dequantized values. P is rounded to
+// e4m3 for the P.V product (P <= 2^8 by the lazy rescale, inside e4m3's
+// range); O = scale_v * acc / l is written as bf16.
+// ===========================================================================
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef int intx2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) intx2 lds_intx2;
+
+constexpr int kE8M0One = 127;  // block scale 2^0 for the scaled MFMA
+
+template <int D, int BLK>
+struct Shape8 {
+  static constexpr int NW = BLK / 32;     // waves (32 query rows each)
+  static constexpr int NT = NW * 64;
+  static constexpr int KB = BLK / 32;     // 32-key blocks of S^T
+  static constexpr int DS = D / 64;       // 64-wide d steps of S^T = K Q^T
+  static constexpr int MB = D / 32;       // 32-wide d blocks of O^T
+  static constexpr int KS = BLK / 64;     // 64-key steps of O^T += V^T P^T
+  static constexpr int CH = D / 16;       // 16-byte granules per row (1 byte per element)
+  static constexpr int GRAN = BLK * CH;
+  static constexpr int DMA = GRAN / NT;
+  static_assert(GRAN % NT == 0, "tile must split evenly over the threads");
+  static_assert(CH == 4 || CH == 8, "head_dim 64 or 128");
+};
+
+// K rows: the 16 rows one ds_read_b128 pass serves read the same granule
+// column; XOR with (row / (16 / CH)) spreads them over all banks.
+template <int CH>
+__device__ __forceinline__ int swz_k8(int row) { return (row / (16 / CH)) & (CH - 1); }
+
+// V rows: a ds_read_b64_tr_b8 pass reads 32 contiguous bytes (two granules)
+// from each of 8 rows {0..3, 8..11} (+4 for the other half-wave); an even
+// XOR keeps each granule pair together and puts the 8 rows on distinct banks.
+template <int CH>
+__device__ __forceinline__ int swz_v8(int row) {
+  if constexpr (CH == 8) {
+    return 2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
+  } else {
+    return 2 * ((row >> 3) & 1);
+  }
+}
+
+// global -> LDS copy of one BLK x D e4m3 tile (same scheme as dma_load).
+template <int D, int BLK, bool IS_V>
+__device__ __forceinline__ void dma_load8(const uint8_t* head, uint32_t bytes, uint8_t* lds, int row0,
+                                          int64_t stride_tok, int wave, int lane) {
+  using SH = Shape8<D, BLK>;
+  constexpr int RPI = 64 / SH::CH;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)head, 0, bytes, kBufferFlags);
+  const int lrow = lane / SH::CH;
+#pragma unroll
+  for (int i = 0; i < SH::DMA; ++i) {
+    const int rin = RPI * (i * SH::NW + wave);
+    const int row = rin + lrow;
+    const int chunk = (lane % SH::CH) ^ (IS_V ? swz_v8<SH::CH>(row) : swz_k8<SH::CH>(row));
+    const uint32_t voff = (uint32_t)((int64_t)lrow * stride_tok + chunk * 16);
+    const uint32_t soff = (uint32_t)((int64_t)(row0 + rin) * stride_tok);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + (i * SH::NW + wave) * 1024), 16, voff, soff, 0,
+                                             0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t head_extent8(int rows, int64_t stride_tok) {
+  return rows > 0 ? (uint32_t)((int64_t)(rows - 1) * stride_tok + D) : 0u;
+}
+
+// A operand of S^T = K Q^T (32x32x64): key 32 kb + l32, d bytes [64 s + 32 hl, +32)
+template <class SH>
+__device__ __forceinline__ intx8 read_k8(const uint8_t* k_lds, int kb, int s, int l32, int hl) {
+  const int row = 32 * kb + l32;
+  const int g0 = 4 * s + 2 * hl;
+  const int sw = swz_k8<SH::CH>(row);
+  const uint4 a = *reinterpret_cast<const uint4*>(k_lds + (row * SH::CH + (g0 ^ sw)) * 16);
+  const uint4 b = *reinterpret_cast<const uint4*>(k_lds + (row * SH::CH + ((g0 + 1) ^ sw)) * 16);
+  return intx8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+
+// A operand of O^T += V^T P^T for 64-key step s, d block mb: four transposing
+// byte reads give lane l the 32 keys (in P's slot order) of column
+// d = 32 mb + l % 32. Read t covers slots 8t..8t+7: this lane supplies row
+// tr_off[t] / row bytes of the step, granule 2 mb + g (stored at position
+// (2 mb + g) ^ tr_sw[t]; the XOR is even, so g stays the low bit) and byte
+// 8 c of it; tr_off[t] holds the row, g and c parts.
+template <class SH>
+__device__ __forceinline__ intx8 read_vt8(const uint8_t* v_lds, int s, int mb, const int* tr_off,
+                                          const int* tr_sw) {
+  intx8 r;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint8_t* ptr = v_lds + s * 64 * (SH::CH * 16) + tr_off[t] + ((2 * mb) ^ tr_sw[t]) * 16;
+    const intx2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_intx2*)ptr);
+    r[2 * t] = x[0];
+    r[2 * t + 1] = x[1];
+  }
+  return r;
+}
+
+template <int D, int BLK, bool CALIB>
+__global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_fp8(const LaunchParams p) {
+  using SH = Shape8<D, BLK>;
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[BLK * D];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[BLK * D];
+  __shared__ uint64_t vote[SH::NW];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  const int G = p.total_wg;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int L = xcd * (G >> 3) + min(xcd, G & 7) + (bid >> 3);
+  int b = 0;
+  while (b + 1 < p.nseq && p.wg_start[b + 1] <= L) ++b;
+  const int tok0 = p.tok_start[b];
+  const int S = p.tok_start[b + 1] - tok0;
+  const int nQ = (S + BLK - 1) / BLK;
+  const int rem = L - p.wg_start[b];
+  const int h = rem / nQ;
+  const int qb = p.causal ? nQ - 1 - (rem - h * nQ) : rem - h * nQ;
+  const int nK = p.causal ? qb + 1 : nQ;
+  const int row = p.wg_start[b] + h * nQ + qb;
+  const int H = p.num_heads;
+  const int64_t head_off = (int64_t)tok0 * p.stride_tok + (int64_t)h * p.stride_head;  // elements = bytes
+  const uint8_t* q8 = reinterpret_cast<const uint8_t*>(p.q);
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) + head_off;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) + head_off;
+  const uint32_t head_bytes = head_extent8<D>(S, p.stride_tok);
+
+  dma_load8<D, BLK, false>(kbase, head_bytes, k_lds, 0, p.stride_tok, wave, lane);
+
+  // Q fragment: B operand of S^T = K Q^T: query qrow, d bytes [64 s + 32 hl, +32)
+  const int qrow = qb * BLK + wave * 32 + l32;
+  const bool qvalid = qrow < S;
+  intx8 qf[SH::DS];
+  {
+    const uint8_t* qp = q8 + head_off + (int64_t)(qvalid ? qrow : 0) * p.stride_tok + 32 * hl;
+#pragma unroll
+    for (int s = 0; s < SH::DS; ++s) {
+      uint4 a = make_uint4(0u, 0u, 0u, 0u), c = make_uint4(0u, 0u, 0u, 0u);
+      if (qvalid) {
+        a = *reinterpret_cast<const uint4*>(qp + 64 * s);
+        c = *reinterpret_cast<const uint4*>(qp + 64 * s + 16);
+      }
+      qf[s] = intx8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z, (int)c.w};
+    }
+  }
+
+  const float c2 = p.scale_log2;  // includes scale_q * scale_k
+  const float t = CALIB ? 0.0f : p.t_bh[b * H + h];
+  const int ncal = CALIB ? p.ncal : 0;
+  int ncount = 0;
+  float m_true = -INFINITY, m_use = -INFINITY, l = 0.0f;
+  floatx16 acc[SH::MB];
+#pragma unroll
+  for (int mb = 0; mb < SH::MB; ++mb) acc[mb] = floatx16{};
+  int skipped = 0;
+
+  // V^T transposing-read sources: source lane (2e + c) of each 16-lane group
+  // supplies key slot e of the read, columns 16 g + 8 c of the 32-wide block.
+  int tr_off[4], tr_sw[4];
+  {
+    const int e = (lane & 15) >> 1, c = lane & 1, g = (lane & 31) >> 4;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int key = 32 * (tt >> 1) + 16 * (tt & 1) + 8 * (e >> 2) + 4 * hl + (e & 3);
+      tr_off[tt] = key * (SH::CH * 16) + g * 16 + 8 * c;
+      tr_sw[tt] = swz_v8<SH::CH>(key);
+    }
+  }
+
+  wait_dma();
+  __syncthreads();
+
+  for (int j = 0; j < nK; ++j) {
+    const int nvalid = min(BLK, S - j * BLK);
+    floatx16 sc[SH::KB];
+#pragma unroll
+    for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
+#pragma unroll
+    for (int s = 0; s < SH::DS; ++s) {
+      intx8 ka[SH::KB];
+#pragma unroll
+      for (int kb = 0; kb < SH::KB; ++kb) ka[kb] = read_k8<SH>(k_lds, kb, s, l32, hl);
+#pragma unroll
+      for (int kb = 0; kb < SH::KB; ++kb)
+        sc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[kb], qf[s], sc[kb], 0, 0, 0, kE8M0One, 0,
+                                                                 kE8M0One);
+    }
+    const int kmax = (p.causal && j == qb) ? min(nvalid, wave * 32 + l32 + 1) : nvalid;
+    if (p.causal ? j == qb : nvalid < BLK) {
+#pragma unroll
+      for (int kb = 0; kb < SH::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (key >= kmax) sc[kb][r] = -INFINITY;
+        }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < SH::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    const float rowmax = xhalf_max(mx) * c2;
+    const float x = qvalid ? rowmax - m_true : -INFINITY;
+    if constexpr (CALIB) {
+      uint64_t bits = 0;
+      for (int k = 0; k < ncal; ++k)
+        if (wave_any(x >= p.cal_t[k])) bits |= 1ull << k;
+      if (lane == 0) vote[wave] = bits;
+    } else {
+      const bool kw = wave_any(x >= t);
+      if (lane == 0) vote[wave] = kw ? 1ull : 0ull;
+    }
+    __syncthreads();
+
+    uint64_t all = vote[0];
+#pragma unroll
+    for (int w = 1; w < SH::NW; ++w) all |= vote[w];
+    bool keep;
+    if constexpr (CALIB) {
+      if (lane < ncal) ncount += ((all >> lane) & 1ull) ? 0 : 1;
+      keep = true;
+    } else {
+      keep = __builtin_amdgcn_readfirstlane(all != 0 ? 1 : 0) != 0;
+      skipped += keep ? 0 : 1;
+      if (p.tile_mask != nullptr && tid == 0)
+        p.tile_mask[((int64_t)((p.seq_abs0 + b) * H + h) * p.mask_nq + qb) * p.mask_nk + j] = keep ? 0 : 1;
+    }
+
+    if (j + 1 < nK) dma_load8<D, BLK, false>(kbase, head_bytes, k_lds, (j + 1) * BLK, p.stride_tok, wave, lane);
+    intx8 pb[SH::KS];
+    if (keep) {
+      dma_load8<D, BLK, true>(vbase, head_bytes, v_lds, j * BLK, p.stride_tok, wave, lane);
+      m_true = fmaxf(m_true, rowmax);
+      if (wave_any(rowmax > m_use + kRescaleSlack)) {
+        const float m_new = fmaxf(m_use, rowmax);
+        const float alpha = fast_exp2(m_use - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < SH::MB; ++mb) acc[mb] *= alpha;
+        m_use = m_new;
+      }
+      const float nm = -m_use;
+      // P^T for 64-key step s: byte 16 u + r is score register r of key block 2 s + u
+#pragma unroll
+      for (int s = 0; s < SH::KS; ++s)
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int kb = 2 * s + (w >> 2);
+          const int r0 = 4 * (w & 3);
+          float e0 = fast_exp2(fmaf(sc[kb][r0], c2, nm));
+          float e1 = fast_exp2(fmaf(sc[kb][r0 + 1], c2, nm));
+          float e2 = fast_exp2(fmaf(sc[kb][r0 + 2], c2, nm));
+          float e3 = fast_exp2(fmaf(sc[kb][r0 + 3], c2, nm));
+          l += (e0 + e1) + (e2 + e3);
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, word, true);
+          pb[s][w] = word;
+        }
+    }
+    wait_dma();
+    __syncthreads();
+
+    if (keep) {
+#pragma unroll
+      for (int s = 0; s < SH::KS; ++s) {
+        intx8 va[SH::MB];
+#pragma unroll
+        for (int mb = 0; mb < SH::MB; ++mb) va[mb] = read_vt8<SH>(v_lds, s, mb, tr_off, tr_sw);
+#pragma unroll
+        for (int mb = 0; mb < SH::MB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[mb], pb[s], acc[mb], 0, 0, 0, kE8M0One, 0,
+                                                                    kE8M0One);
+      }
+    }
+  }
+
+  const float inv = p.v_scale / xhalf_sum(l);
+  if (qvalid) {
+    uint16_t* op = p.o + head_off + (int64_t)qrow * p.stride_tok;
+#pragma unroll
+    for (int mb = 0; mb < SH::MB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const floatx4 f = {acc[mb][4 * g] * inv, acc[mb][4 * g + 1] * inv, acc[mb][4 * g + 2] * inv,
+                           acc[mb][4 * g + 3] * inv};
+        const bf16x4 o4 = __builtin_convertvector(f, bf16x4);
+        *reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * g + 4 * hl) = o4;
+      }
+  }
+  if constexpr (CALIB) {
+    if (wave == 0 && lane < ncal) p.counts[(p.wg_abs0 + row) * ncal + lane] = ncount;
+    if (tid == 0) p.tiles[p.wg_abs0 + row] = nK;
+  } else {
+    if (tid == 0) {
+      const int64_t bh = (int64_t)(p.seq_abs0 + b) * H + h;
+      if (p.skipped_bh != nullptr) atomicAdd((unsigned long long*)&p.skipped_bh[bh], (unsigned long long)skipped);
+      if (p.total_bh != nullptr) atomicAdd((unsigned long long*)&p.total_bh[bh], (unsigned long long)nK);
+    }
+  }
+}
+
 __global__ void fill_u8_kernel(uint8_t* dst, int64_t n, uint8_t value) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     dst[i] = value;
@@ -411,8 +724,13 @@ __global__ void fill_u64_kernel(uint64_t* dst, int64_t n) {
 
 template <int D, int BLK, bool CALIB>
 int launch(const LaunchParams& p, hipStream_t stream) {
-  using SH = Shape<D, BLK>;
-  hipLaunchKernelGGL((fwd_kernel<D, BLK, CALIB>), dim3(p.total_wg), dim3(SH::NT), 0, stream, p);
+  if (p.fp8) {
+    using SH = Shape8<D, BLK>;
+    hipLaunchKernelGGL((fwd_kernel_fp8<D, BLK, CALIB>), dim3(p.total_wg), dim3(SH::NT), 0, stream, p);
+  } else {
+    using SH = Shape<D, BLK>;
+    hipLaunchKernelGGL((fwd_kernel<D, BLK, CALIB>), dim3(p.total_wg), dim3(SH::NT), 0, stream, p);
+  }
   return (int)hipGetLastError();
 }
 

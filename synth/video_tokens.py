@@ -97,6 +97,64 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+E4M3_MAX = 448.0
+
+
+def e4m3_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact value of each OCP e4m3 ("e4m3fn") byte: 1 sign, 4 exponent (bias 7),
+    3 mantissa bits, subnormals at exponent 0, NaN at S.1111.111, no infinities."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int32)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = (b & 7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 15) & ((b & 7) == 7), np.nan, val)
+    return (sign * val).astype(np.float32)
+
+
+_E4M3_POS = e4m3_bits_to_f32(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)  # codes 0..126, ascending
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest e4m3 value (ties to the even code), saturating at +-448."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 126)  # first code with value >= a
+    lo = np.clip(hi - 1, 0, 126)
+    dlo = a - _E4M3_POS[lo]
+    dhi = _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(a == _E4M3_POS[hi], hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def quantize_e4m3(values: np.ndarray):
+    """Per-tensor e4m3 quantization: scale = max|x| / 448; returns (bytes, scale)."""
+    amax = float(np.max(np.abs(values))) if values.size else 0.0
+    scale = amax / E4M3_MAX if amax > 0 else 1.0
+    return f32_to_e4m3_bits(np.asarray(values, np.float64) / scale), scale
+
+
+def make_fp8_inputs(x: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
+    """e4m3 versions of bf16 inputs from `make_inputs`: q8/k8/v8 bytes [T,H,D]
+    and their per-tensor dequantization scales (value = code * scale).
+    Each bf16 bit pattern is converted once (a 65,536-entry table), which is
+    the same as converting every element."""
+    out = {"cu_seqlens": x["cu_seqlens"]}
+    with np.errstate(invalid="ignore"):
+        all_bf16 = bf16_bits_to_f32(np.arange(65536, dtype=np.uint32).astype(np.uint16)).astype(np.float64)
+    for n in ("q", "k", "v"):
+        used = np.zeros(65536, dtype=bool)
+        used[np.asarray(x[n]).ravel()] = True
+        vals = all_bf16[used]
+        amax = float(np.max(np.abs(vals[np.isfinite(vals)]))) if vals.size else 0.0
+        scale = amax / E4M3_MAX if amax > 0 else 1.0
+        lut = f32_to_e4m3_bits(np.where(np.isfinite(all_bf16), all_bf16, 0.0) / scale)
+        out[n + "8"] = lut[x[n]]
+        out["scale_" + n] = scale
+    return out
+
+
 def grid_positions(grid: Sequence[int]) -> np.ndarray:
     """(S, 3) float64 grid coordinates (f, r, c) in frame-major token order."""
     f, h, w = grid

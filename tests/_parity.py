@@ -123,3 +123,29 @@ def sample_qblocks(cu, H: int, block: int, heads: Sequence[int], per_head: int, 
                 picks.add(int(rng.integers(nq)))
             out += [(b, h, i) for i in sorted(picks)]
     return out
+
+
+# ---- e4m3 (FP8) path ------------------------------------------------------------------
+# The kernel rounds P to e4m3 for the P.V product. With P = 2^(s - m_base),
+# where m_base lies within 2^8 of the row's running maximum, a value in the
+# normal range moves by at most 2^-4 of itself. A subnormal value moves by at
+# most 2^-10, and a flushed one by itself. So row r's output moves by at most
+#   max|v| * sum_j max(2^-4 p_j, min(p_j, 2^-10)) / sum_j p_j,
+# with p_j = 2^(s_j - max kept s) over the kept keys. On top of that come the
+# bf16 rounding of O (2^-9 relative) and fp32 accumulation noise.
+FP8_NOISE = 2e-3
+
+
+def fp8_row_bound(qf: np.ndarray, kf: np.ndarray, vf: np.ndarray, kept_cols: np.ndarray, scale: float,
+                  o_ref: np.ndarray, causal_row0=None) -> np.ndarray:
+    """Per-row output bound of the e4m3 P.V product (see above), fp64.
+    qf [R, D] rows, kf/vf [S, D] of one head (dequantized), kept_cols [S] bool."""
+    s = (qf @ kf.T) * (scale / math.log(2.0))
+    if causal_row0 is not None:
+        rows = causal_row0 + np.arange(s.shape[0])[:, None]
+        s = np.where(np.arange(s.shape[1])[None, :] <= rows, s, -np.inf)
+    s = np.where(kept_cols[None, :], s, -np.inf)
+    p = np.exp2(s - s.max(axis=1, keepdims=True))
+    err = np.maximum(2.0 ** -4 * p, np.minimum(p, 2.0 ** -10))
+    vmax = np.abs(vf).max()
+    return vmax * err.sum(1) / p.sum(1) + 2.0 ** -8 * np.abs(o_ref).max(1) + FP8_NOISE

@@ -352,3 +352,129 @@ def test_causal_calibration_counts():
 def test_causal_headline_sampled_parity():
     fr = _sampled_parity(CONFIGS["headline"], [0.0, 8e-3], heads=[0, 39], per_head=3, causal=True)
     assert fr[0] == 0.0 and fr[1] > 0.1
+
+
+# ---- FP8 (e4m3) variant -------------------------------------------------------------
+def _fp8_inputs(cfg):
+    import torch
+    from synth import e4m3_bits_to_f32, make_fp8_inputs
+    x = make_inputs(cfg)
+    f = make_fp8_inputs(x)
+    xd = {n: torch.from_numpy(np.ascontiguousarray(f[n + "8"])).cuda() for n in ("q", "k", "v")}
+    scales = (f["scale_q"], f["scale_k"], f["scale_v"])
+    xf = {n: e4m3_bits_to_f32(f[n + "8"]).astype(np.float64) * f["scale_" + n] for n in ("q", "k", "v")}
+    return xd, xf, scales, x["cu_seqlens"]
+
+
+def _fp8_forward(xd, cu, lam, block, scales, causal=False, mask=True):
+    import torch
+    import skip_softmax_video_amd as ssa
+    B = len(cu) - 1
+    T, H, D = xd["q"].shape
+    skipped = torch.zeros(B * H, dtype=torch.int64, device="cuda")
+    total = torch.zeros(B * H, dtype=torch.int64, device="cuda")
+    prob, _ = ssa.make_problem(xd["q"], cu, block, scales=scales)
+    nq, nk = ssa.tile_mask_dims(prob)
+    tm = torch.empty((B, H, nq, nk), dtype=torch.uint8, device="cuda") if mask else None
+    o = ssa.attn_fwd(xd["q"], xd["k"], xd["v"], cu, lam, block=block, skipped=skipped, total=total,
+                     tile_mask=tm, causal=causal, scales=scales)
+    torch.cuda.synchronize()
+    return (o.float().cpu().numpy(), skipped.cpu().numpy().reshape(B, H), total.cpu().numpy().reshape(B, H),
+            None if tm is None else tm.cpu().numpy())
+
+
+def _fp8_full_parity(cfg, lam, causal=False):
+    from tests._parity import fp8_row_bound
+    xd, xf, scales, cu = _fp8_inputs(cfg)
+    H, blk = cfg.num_heads, cfg.block
+    log(f"[{cfg.name} fp8] lambda={lam} causal={causal} scales={tuple(round(s, 6) for s in scales)}")
+    o, sk, tot, mask = _fp8_forward(xd, cu, lam, blk, scales, causal=causal)
+    t = t_matrix(cu, H, lam, "lambda")
+    ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk, causal=causal)
+    band, mism = compare_masks(mask, ref, t, osk.workgroups(cu, H, blk))
+    forced = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk, forced_mask=mask, causal=causal)
+    np.testing.assert_array_equal(sk, (mask == osk.TILE_SKIPPED).sum(axis=(2, 3)))
+    np.testing.assert_array_equal(tot, ref["total"])
+    scale = osk.default_sm_scale(cfg.head_dim)
+    worst_ratio, mean_abs = 0.0, []
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        if s1 == s0:
+            continue
+        for h in range(H):
+            for i in range(osk.n_tiles(s1 - s0, blk)):
+                r0, r1 = i * blk, min(s1 - s0, (i + 1) * blk)
+                kept_tiles = mask[b, h, i] == osk.TILE_KEPT
+                kept_cols = np.repeat(kept_tiles, blk)[: s1 - s0]
+                o_ref = forced["o"][s0 + r0:s0 + r1, h]
+                bound = fp8_row_bound(xf["q"][s0 + r0:s0 + r1, h], xf["k"][s0:s1, h], xf["v"][s0:s1, h],
+                                      kept_cols, scale, o_ref, causal_row0=r0 if causal else None)
+                err = np.abs(o[s0 + r0:s0 + r1, h] - o_ref).max(1)
+                assert np.all(err <= bound), f"fp8 output outside its bound at {(b, h, i)}: {err.max():.3e}"
+                worst_ratio = max(worst_ratio, float((err / bound).max()))
+                mean_abs.append(np.abs(o[s0 + r0:s0 + r1, h] - o_ref).mean())
+    log(f"  skipped {sk.sum()}/{tot.sum()} band {band} band-mismatch {mism} mean-abs {np.mean(mean_abs):.2e} "
+        f"worst err/bound {worst_ratio:.3f}")
+    return sk, tot
+
+
+@pytest.mark.parametrize("lam", [0.0, 1e-2, 1.0])
+def test_fp8_tiny_parity(lam):
+    sk, tot = _fp8_full_parity(CONFIGS["tiny"], lam)
+    assert (sk.sum() == 0) == (lam == 0.0)
+
+
+@pytest.mark.parametrize("lam,causal", [(0.0, False), (1e-2, False), (1e-2, True)])
+def test_fp8_ragged_d128_parity(lam, causal):
+    _fp8_full_parity(RAGGED, lam, causal=causal)
+
+
+def test_fp8_calibration_counts_match_forward():
+    import torch
+    import skip_softmax_video_amd as ssa
+    xd, xf, scales, cu = _fp8_inputs(RAGGED)
+    lams = np.geomspace(1e-5, 0.7, 6)
+    o_cal, counts, tiles = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, lams, block=RAGGED.block,
+                                              scales=scales)
+    torch.cuda.synchronize()
+    counts = counts.cpu().numpy()
+    wgs = osk.workgroups(cu, RAGGED.num_heads, RAGGED.block)
+    o0, _, _, _ = _fp8_forward(xd, cu, 0.0, RAGGED.block, scales, mask=False)
+    np.testing.assert_array_equal(o_cal.float().cpu().numpy(), o0)
+    for kk, lam in enumerate(lams):
+        _, _, _, mask = _fp8_forward(xd, cu, lam, RAGGED.block, scales)
+        per_wg = np.array([(mask[b, h, i] == osk.TILE_SKIPPED).sum() for (b, h, i) in wgs])
+        np.testing.assert_array_equal(counts[:, kk], per_wg)
+
+
+def test_fp8_headline_sampled_parity():
+    """Full-size e4m3 launch at the headline shape; skip bits and outputs
+    checked on sampled Q-blocks against the oracle on the dequantized inputs."""
+    from tests._parity import fp8_row_bound
+    cfg = CONFIGS["headline"]
+    xd, xf, scales, cu = _fp8_inputs(cfg)
+    H, blk = cfg.num_heads, cfg.block
+    scale = osk.default_sm_scale(cfg.head_dim)
+    qbs = sample_qblocks(cu, H, blk, [0, 39], 3, seed=cfg.seed)
+    S = int(cu[1])
+    for lam in (0.0, 8e-3):
+        log(f"[headline fp8] lambda={lam}: GPU forward (full launch)")
+        o, sk, tot, mask = _fp8_forward(xd, cu, lam, blk, scales)
+        t = t_matrix(cu, H, lam, "lambda")
+        assert np.all(tot == osk.n_tiles(S, blk) ** 2)
+        worst = 0.0
+        for (b, h, i) in qbs:
+            kh, vh = xf["k"][:, h], xf["v"][:, h]
+            r0, r1 = i * blk, min(S, (i + 1) * blk)
+            qh = xf["q"][r0:r1, h]
+            d, _ = osk.tile_stats_fast(qh, kh, blk, scale)
+            near = np.abs(d - t[b, h]) <= 1e-3
+            gpu_skip = mask[b, h, i] == osk.TILE_SKIPPED
+            assert not np.any((gpu_skip != (d < t[b, h])) & ~near), f"skip mismatch at {(b, h, i)}"
+            ref = osk.skip_softmax_qblock(qh, kh, vh, t[b, h], blk, scale, forced_skip=gpu_skip)
+            kept_cols = np.repeat(~gpu_skip, blk)[:S]
+            bound = fp8_row_bound(qh, kh, vh, kept_cols, scale, ref["o"])
+            err = np.abs(o[r0:r1, h] - ref["o"]).max(1)
+            assert np.all(err <= bound), f"fp8 output outside its bound at {(b, h, i)}: {err.max():.3e}"
+            worst = max(worst, float((err / bound).max()))
+        log(f"  sparsity {sk.sum() / tot.sum():.4f} worst err/bound {worst:.3f}")

@@ -127,6 +127,11 @@ FAKE = 1 << 20  # aligned, never dereferenced: validation fails first
     (dict(stride_token=100), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
     (dict(sm_scale=-1.0), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
     (dict(causal=2), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(dtype=2), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(dtype=1, scale_q=1.0, scale_k=1.0, scale_v=0.0), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(dtype=1, scale_q=1.0, scale_k=float("inf"), scale_v=1.0), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(dtype=1, scale_q=1.0, scale_k=1.0, scale_v=1.0, stride_token=264, stride_head=136),
+     (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),                          # e4m3 rows must be 16-byte aligned
     (dict(causal=-1), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
     (dict(), (0, [1.5]), ssa.SSA_ERR_THRESHOLD_RANGE),
     (dict(), (0, [float("nan")]), ssa.SSA_ERR_THRESHOLD_RANGE),
