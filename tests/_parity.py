@@ -109,6 +109,22 @@ def compare_outputs(o_gpu: np.ndarray, o_ref: np.ndarray, rows: Optional[np.ndar
     return mx, mean
 
 
+def compare_outputs_derived(o_gpu: np.ndarray, o_ref: np.ndarray, vmax: float):
+    """Output check for plain N(0, s^2) edge-case inputs, whose sharp rows push
+    |O| up to max|V|, beyond the video workloads the 2e-2 bound is stated for.
+    Bound per element:
+    - the bf16 rounding of P (2^-9 relative, times max|V|);
+    - plus the rounding of O (2^-9 relative);
+    - plus accumulation noise; each rounding term is taken twice for margin."""
+    sel = ~np.isnan(o_ref)
+    diff = np.abs(o_gpu[sel] - o_ref[sel])
+    tol = 2.0 ** -8 * vmax + 2.0 ** -8 * np.abs(o_ref[sel]) + 1e-3
+    assert np.all(np.isfinite(o_gpu[sel])), "non-finite GPU output"
+    assert np.all(diff <= tol), f"output outside the derived bound: max-abs {diff.max():.3e}"
+    assert diff.mean() <= O_MEAN_ABS, f"mean-abs {diff.mean():.3e}"
+    return float(diff.max()), float(diff.mean())
+
+
 def sample_qblocks(cu, H: int, block: int, heads: Sequence[int], per_head: int, seed: int):
     """Deterministic sample of Q-blocks: first, last (often partial) and random ones."""
     rng = np.random.default_rng(seed)

@@ -12,8 +12,8 @@ from oracle import calibration as oc
 from oracle import skip_softmax as osk
 from synth import CONFIGS, make_inputs
 from synth.video_tokens import VideoTokenConfig
-from tests._parity import (compare_masks, compare_outputs, gpu_forward, log, sample_qblocks, t_matrix,
-                           to_device, to_f64)
+from tests._parity import (compare_masks, compare_outputs, compare_outputs_derived, gpu_forward, log,
+                           sample_qblocks, t_matrix, to_device, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -478,3 +478,62 @@ def test_fp8_headline_sampled_parity():
             assert np.all(err <= bound), f"fp8 output outside its bound at {(b, h, i)}: {err.max():.3e}"
             worst = max(worst, float((err / bound).max()))
         log(f"  sparsity {sk.sum() / tot.sum():.4f} worst err/bound {worst:.3f}")
+
+
+# ---- launch splitting, limits and degenerate shapes ---------------------------------
+def test_launch_splitting_many_sequences_per_head_thresholds():
+    """40 sequences x 16 heads: more than 32 sequences and 512 (sequence, head)
+    thresholds per launch, so the host splits the batch into several launches.
+    Per-head scale factors (lambda = sf / S_b) make every launch's threshold
+    table different; one sequence is empty."""
+    from synth.video_tokens import make_random_inputs
+    rng = np.random.default_rng(21)
+    lens = [int(x) for x in rng.integers(64, 300, 40)]  # >= 64 keys: lambda = sf / S stays <= 1
+    lens[17] = 0
+    H, D, blk = 16, 64, 64
+    x = make_random_inputs(lens, H, D, seed=22, scale=1.5)
+    xd = {n: to_device(x[n]) for n in ("q", "k", "v")}
+    xf = {n: to_f64(x[n]) for n in ("q", "k", "v")}
+    cu = x["cu_seqlens"]
+    sf = np.concatenate([[0.0], np.geomspace(0.5, 60.0, H - 1)])
+    log(f"[split] B={len(lens)} H={H} total tokens {int(cu[-1])}")
+    o, sk, tot, mask = gpu_forward(xd, cu, sf, "scale_factor", blk)
+    t = t_matrix(cu, H, sf, "scale_factor")
+    ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk)
+    band, mism = compare_masks(mask, ref, t, osk.workgroups(cu, H, blk))
+    forced = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk, forced_mask=mask)
+    compare_outputs_derived(o, forced["o"], np.abs(xf["v"]).max())
+    np.testing.assert_array_equal(tot, ref["total"])
+    assert sk[:, 0].sum() == 0 and sk.sum() > 0
+    log(f"  skipped {sk.sum()}/{tot.sum()} band {band} band-mismatch {mism}")
+
+
+def test_max_heads_and_tiny_sequences():
+    """512 heads (the limit), sequences of 1, 2 and 129 tokens."""
+    from synth.video_tokens import make_random_inputs
+    lens = [1, 2, 129]
+    H, D, blk = 512, 64, 64
+    x = make_random_inputs(lens, H, D, seed=23, scale=2.0)
+    xd = {n: to_device(x[n]) for n in ("q", "k", "v")}
+    xf = {n: to_f64(x[n]) for n in ("q", "k", "v")}
+    cu = x["cu_seqlens"]
+    o, sk, tot, mask = gpu_forward(xd, cu, 0.5, "lambda", blk)
+    t = t_matrix(cu, H, 0.5, "lambda")
+    ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk, fast=True)
+    compare_masks(mask, ref, t, osk.workgroups(cu, H, blk))
+    forced = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk, forced_mask=mask, fast=True)
+    compare_outputs_derived(o, forced["o"], np.abs(xf["v"]).max())
+    np.testing.assert_array_equal(tot, ref["total"])
+    import skip_softmax_video_amd as ssa
+    with pytest.raises(ssa.SSAError):
+        x2 = make_random_inputs([8], 513, 64, seed=1)
+        d2 = {n: to_device(x2[n]) for n in ("q", "k", "v")}
+        ssa.attn_fwd(d2["q"], d2["k"], d2["v"], x2["cu_seqlens"], 0.1, block=64)
+
+
+@pytest.mark.parametrize("head_dim,block", [(64, 64), (64, 128), (128, 64)])
+def test_fp8_other_tile_shapes(head_dim, block):
+    cfg = VideoTokenConfig("mixed8", ((4, 13, 20), (1, 5, 9)), num_heads=2, head_dim=head_dim, sigma=0.5,
+                           block=block, seed=9)
+    sk, _ = _fp8_full_parity(cfg, 1e-1)
+    assert sk.sum() > 0
