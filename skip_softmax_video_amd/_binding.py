@@ -307,6 +307,10 @@ class CalibrationPool:
                             visited=self._visited.ctypes.data_as(P(ctypes.c_int64)))
 
     def add(self, cu_seqlens, num_heads: int, block: int, counts, tiles) -> None:
+        """Add one calibration pass (host or device counts [num_wg, n] and tiles [num_wg]).
+        Only the sequence lengths, heads and block size of the pass matter here."""
+        if hasattr(counts, "cpu"):
+            counts, tiles = counts.cpu().numpy(), tiles.cpu().numpy()
         cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
         c = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
         t = np.ascontiguousarray(np.asarray(tiles, dtype=np.int32))

@@ -108,6 +108,7 @@ extern "C" int ssa_calibration_pool_add(const ssa_problem* p, const int32_t* cou
       pool->n_groups > pool->max_groups)
     return SSA_ERR_INVALID_ARG;
   if (pool->n_lambda != 0 && pool->n_lambda != n) return SSA_ERR_INVALID_ARG;
+  if (p->cu_seqlens[0] != 0) return SSA_ERR_INVALID_ARG;
   if (pool->max_groups > 0 && (pool->seq_k == nullptr || pool->skipped == nullptr || pool->visited == nullptr))
     return SSA_ERR_INVALID_ARG;
   // map every non-empty sequence to a group first, so a full pool leaves everything unchanged

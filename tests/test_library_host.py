@@ -309,6 +309,8 @@ def test_pool_errors_leave_it_unchanged():
     cu3, counts3, tiles3 = _random_pass(rng, 2, 64, 3, [100])  # wrong threshold count
     with pytest.raises(ssa.SSAError):
         pool.add(cu3, 2, 64, counts3, tiles3)
+    with pytest.raises(ssa.SSAError):  # cu_seqlens must start at 0
+        pool.add(np.asarray(cu) + 5, 2, 64, counts, tiles)
     after = pool.groups
     assert list(after) == list(before)
     for k in before:
