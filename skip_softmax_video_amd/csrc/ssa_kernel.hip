@@ -40,8 +40,10 @@
 //     +inf and the first tile is always kept). A wave keeps the tile if any
 //     valid lane has x >= t (one ballot); the work-group ORs the waves'
 //     flags through LDS, so d = max_r x_r < t exactly when nobody keeps.
-//     The calibration instantiation takes one ballot per threshold, never
-//     skips, and writes one row of counts per work-group (no atomics).
+//     The calibration instantiation never skips: each wave reduces x to its
+//     maximum (DPP), the work-group takes d = the maximum over waves, and
+//     lane k (holding threshold k) counts d < t_k; one row of counts per
+//     work-group is written at the end (no atomics).
 //   * V_j is fetched only when the vote kept the tile, issued right after
 //     the vote so that it lands while the softmax runs; K_{j+1} is fetched
 //     as soon as every wave is done reading K_j.
@@ -177,12 +179,30 @@ __device__ __forceinline__ bf16x8 read_vt(const uint16_t* v_lds, int s, int mb, 
 
 __device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
+// Maximum of x over the wave's 64 lanes (DPP steps within quads, half rows
+// and rows of 16 lanes, then row broadcasts), read back from lane 63 so that
+// it is wave-uniform.
+__device__ __forceinline__ float wave_max(float x) {
+#define SSA_DPP_MAX(CTRL, ROWS)                                                                 \
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), \
+                                                          CTRL, ROWS, 0xF, false)))
+  SSA_DPP_MAX(0xB1, 0xF);   // quad_perm [1, 0, 3, 2]
+  SSA_DPP_MAX(0x4E, 0xF);   // quad_perm [2, 3, 0, 1]
+  SSA_DPP_MAX(0x141, 0xF);  // row_half_mirror
+  SSA_DPP_MAX(0x140, 0xF);  // row_mirror: every lane holds its row's maximum
+  SSA_DPP_MAX(0x142, 0xA);  // row_bcast:15 into rows 1 and 3
+  SSA_DPP_MAX(0x143, 0xC);  // row_bcast:31 into rows 2 and 3: lane 63 holds the maximum
+#undef SSA_DPP_MAX
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 template <int D, int BLK, bool CALIB>
 __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {  // 2*BLK = Shape::NT
   using SH = Shape<D, BLK>;
   __shared__ __attribute__((aligned(1024))) uint16_t k_lds[BLK * D];
   __shared__ __attribute__((aligned(1024))) uint16_t v_lds[BLK * D];
   __shared__ uint64_t vote[SH::NW];
+  __shared__ float dvote[SH::NW];  // calibration: each wave's maximum of x
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps tile addressing scalar
@@ -233,6 +253,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
   const float c2 = p.scale_log2;
   const float t = CALIB ? 0.0f : p.t_bh[b * H + h];
   const int ncal = CALIB ? p.ncal : 0;
+  const float my_t = (CALIB && lane < ncal) ? p.cal_t[lane] : INFINITY;  // lane k holds threshold k
   int ncount = 0;
 
   float m_true = -INFINITY;  // running max of the method (log2 units), updated on kept tiles
@@ -292,27 +313,31 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
     for (int kb = 0; kb < SH::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    const float rowmax = xhalf_max(mx) * c2;
-    const float x = qvalid ? rowmax - m_true : -INFINITY;  // m_true = -inf gives +inf
+    // rounded product, then rounded difference (never fused): the forward and
+    // the calibration instantiations see bit-identical x
+    const float rowmax = __fmul_rn(xhalf_max(mx), c2);
+    const float x = qvalid ? __fsub_rn(rowmax, m_true) : -INFINITY;  // m_true = -inf gives +inf
     if constexpr (CALIB) {
-      uint64_t bits = 0;  // bit k: some row of this wave keeps the tile at threshold k
-      for (int k = 0; k < ncal; ++k)
-        if (wave_any(x >= p.cal_t[k])) bits |= 1ull << k;
-      if (lane == 0) vote[wave] = bits;
+      // d = max over valid rows; "some row has x >= t_k" is exactly d >= t_k
+      const float dw = wave_max(x);
+      if (lane == 0) dvote[wave] = dw;
     } else {
       const bool kw = wave_any(x >= t);
       if (lane == 0) vote[wave] = kw ? 1ull : 0ull;
     }
     __syncthreads();  // votes visible; every wave is done reading K_j and V_{j-1}
 
-    uint64_t all = vote[0];
-#pragma unroll
-    for (int w = 1; w < SH::NW; ++w) all |= vote[w];
     bool keep;
     if constexpr (CALIB) {
-      if (lane < ncal) ncount += ((all >> lane) & 1ull) ? 0 : 1;
+      float d = dvote[0];
+#pragma unroll
+      for (int w = 1; w < SH::NW; ++w) d = fmaxf(d, dvote[w]);
+      ncount += d < my_t ? 1 : 0;  // lanes >= ncal hold +inf and are never written out
       keep = true;
     } else {
+      uint64_t all = vote[0];
+#pragma unroll
+      for (int w = 1; w < SH::NW; ++w) all |= vote[w];
       keep = __builtin_amdgcn_readfirstlane(all != 0 ? 1 : 0) != 0;  // work-group uniform
       skipped += keep ? 0 : 1;
       if (p.tile_mask != nullptr && tid == 0)
@@ -508,6 +533,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_fp8(const LaunchParams 
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds[BLK * D];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds[BLK * D];
   __shared__ uint64_t vote[SH::NW];
+  __shared__ float dvote[SH::NW];  // calibration: each wave's maximum of x
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -558,6 +584,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_fp8(const LaunchParams 
   const float c2 = p.scale_log2;  // includes scale_q * scale_k
   const float t = CALIB ? 0.0f : p.t_bh[b * H + h];
   const int ncal = CALIB ? p.ncal : 0;
+  const float my_t = (CALIB && lane < ncal) ? p.cal_t[lane] : INFINITY;  // lane k holds threshold k
   int ncount = 0;
   float m_true = -INFINITY, m_use = -INFINITY, l = 0.0f;
   floatx16 acc[SH::MB];
@@ -612,27 +639,28 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_fp8(const LaunchParams 
     for (int kb = 0; kb < SH::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    const float rowmax = xhalf_max(mx) * c2;
-    const float x = qvalid ? rowmax - m_true : -INFINITY;
+    const float rowmax = __fmul_rn(xhalf_max(mx), c2);
+    const float x = qvalid ? __fsub_rn(rowmax, m_true) : -INFINITY;
     if constexpr (CALIB) {
-      uint64_t bits = 0;
-      for (int k = 0; k < ncal; ++k)
-        if (wave_any(x >= p.cal_t[k])) bits |= 1ull << k;
-      if (lane == 0) vote[wave] = bits;
+      const float dw = wave_max(x);
+      if (lane == 0) dvote[wave] = dw;
     } else {
       const bool kw = wave_any(x >= t);
       if (lane == 0) vote[wave] = kw ? 1ull : 0ull;
     }
     __syncthreads();
 
-    uint64_t all = vote[0];
-#pragma unroll
-    for (int w = 1; w < SH::NW; ++w) all |= vote[w];
     bool keep;
     if constexpr (CALIB) {
-      if (lane < ncal) ncount += ((all >> lane) & 1ull) ? 0 : 1;
+      float d = dvote[0];
+#pragma unroll
+      for (int w = 1; w < SH::NW; ++w) d = fmaxf(d, dvote[w]);
+      ncount += d < my_t ? 1 : 0;
       keep = true;
     } else {
+      uint64_t all = vote[0];
+#pragma unroll
+      for (int w = 1; w < SH::NW; ++w) all |= vote[w];
       keep = __builtin_amdgcn_readfirstlane(all != 0 ? 1 : 0) != 0;
       skipped += keep ? 0 : 1;
       if (p.tile_mask != nullptr && tid == 0)

@@ -537,3 +537,32 @@ def test_fp8_other_tile_shapes(head_dim, block):
                            block=block, seed=9)
     sk, _ = _fp8_full_parity(cfg, 1e-1)
     assert sk.sum() > 0
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_headline_calibration_counts_equal_forward_skips(fp8):
+    """At the full headline size the calibration pass counts exactly the tiles
+    the forward skips, threshold by threshold (same arithmetic on both sides)."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    cfg = CONFIGS["calib"]
+    if fp8:
+        xd, _, scales, cu = _fp8_inputs(cfg)
+    else:
+        x, xd, cu = _inputs(cfg)
+        scales = None
+    lams = np.geomspace(1e-6, 0.7, 16)
+    _, counts, tiles = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, lams, block=cfg.block, scales=scales)
+    torch.cuda.synchronize()
+    per_lam = counts.sum(0).cpu().numpy()
+    H = cfg.num_heads
+    skipped = torch.zeros(H, dtype=torch.int64, device="cuda")
+    total = torch.zeros(H, dtype=torch.int64, device="cuda")
+    for kk in (0, 5, 8, 12, 15):
+        ssa.attn_fwd(xd["q"], xd["k"], xd["v"], cu, lams[kk], block=cfg.block, skipped=skipped, total=total,
+                     scales=scales)
+        torch.cuda.synchronize()
+        assert int(skipped.sum()) == int(per_lam[kk]), f"lambda {lams[kk]:.3g}: {int(skipped.sum())} vs {per_lam[kk]}"
+        assert int(total.sum()) == int(tiles.sum())
+    log(f"  fp8={fp8}: calibration counts equal forward skips at 5 of 16 thresholds "
+        f"(sparsity {per_lam[0] / int(tiles.sum()):.3f} .. {per_lam[-1] / int(tiles.sum()):.3f})")
