@@ -179,6 +179,16 @@ __device__ __forceinline__ bf16x8 read_vt(const uint16_t* v_lds, int s, int mb, 
 
 __device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
+// Tile row maximum in log2 units (rounded product) and its margin over the
+// running maximum (rounded difference). Never contracted into one FMA, so
+// every instantiation (forward, calibration, bf16, fp8) takes bit-identical
+// skip decisions from the same scores.
+__device__ __forceinline__ void tile_margin(float tile_max, float c2, float m, float& rowmax, float& x) {
+#pragma clang fp contract(off)
+  rowmax = tile_max * c2;
+  x = rowmax - m;
+}
+
 // Maximum of x over the wave's 64 lanes (DPP steps within quads, half rows
 // and rows of 16 lanes, then row broadcasts), read back from lane 63 so that
 // it is wave-uniform.
@@ -313,10 +323,9 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
     for (int kb = 0; kb < SH::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    // rounded product, then rounded difference (never fused): the forward and
-    // the calibration instantiations see bit-identical x
-    const float rowmax = __fmul_rn(xhalf_max(mx), c2);
-    const float x = qvalid ? __fsub_rn(rowmax, m_true) : -INFINITY;  // m_true = -inf gives +inf
+    float rowmax, x;
+    tile_margin(xhalf_max(mx), c2, m_true, rowmax, x);  // m_true = -inf gives x = +inf
+    if (!qvalid) x = -INFINITY;
     if constexpr (CALIB) {
       // d = max over valid rows; "some row has x >= t_k" is exactly d >= t_k
       const float dw = wave_max(x);
@@ -639,8 +648,9 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_fp8(const LaunchParams 
     for (int kb = 0; kb < SH::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    const float rowmax = __fmul_rn(xhalf_max(mx), c2);
-    const float x = qvalid ? __fsub_rn(rowmax, m_true) : -INFINITY;
+    float rowmax, x;
+    tile_margin(xhalf_max(mx), c2, m_true, rowmax, x);
+    if (!qvalid) x = -INFINITY;
     if constexpr (CALIB) {
       const float dw = wave_max(x);
       if (lane == 0) dvote[wave] = dw;
