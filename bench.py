@@ -235,6 +235,24 @@ def main() -> int:
               "tflops_dense_equiv": round(c_flops / (c_ms * 1e-3) / 1e12, 2)}
     log(f"causal: dense {c_dense_ms:.2f} ms, lambda {lam07:.4g} -> {c_ms:.2f} ms (sparsity {c_sp:.4f})")
 
+    # one GPU's share under 8-way head sharding: heads 0..4 of the same tensors
+    # (strided views, no copy), dense and calibrated lambda
+    hs = H // 8
+    q5, k5, v5, o5 = (t[:, :hs, :] for t in (dx["q"], dx["k"], dx["v"], o))
+    sk5, tt5 = skipped[:hs], total[:hs]
+    ssa.attn_fwd(q5, k5, v5, cu, lam07, block=blk, out=o5, skipped=sk5, total=tt5)
+    torch.cuda.synchronize()
+    h_sp = float(sk5.sum()) / float(tt5.sum())
+    shard_fwd = lambda lam: (lambda: ssa.attn_fwd(q5, k5, v5, cu, lam, block=blk, out=o5))
+    h_dense_ms = time_launches(shard_fwd(0.0), 1, max(2, args.steps // 2))
+    h_ms = time_launches(shard_fwd(lam07), 1, max(2, args.steps // 2))
+    h_flops = 4.0 * hs * D * S * S
+    head_shard = {"heads": hs, "achieved_tile_sparsity": round(h_sp, 4), "dense_ms": round(h_dense_ms, 3),
+                  "ms": round(h_ms, 3), "speedup_vs_dense": round(h_dense_ms / h_ms, 3),
+                  "dense_tflops": round(h_flops / (h_dense_ms * 1e-3) / 1e12, 2),
+                  "tflops_dense_equiv": round(h_flops / (h_ms * 1e-3) / 1e12, 2)}
+    log(f"head shard (H={hs}): dense {h_dense_ms:.2f} ms, lambda {lam07:.4g} -> {h_ms:.2f} ms (sparsity {h_sp:.4f})")
+
     # FP8 (e4m3) variant of the same inputs: per-tensor quantized on the host
     from synth import make_fp8_inputs
     log("quantizing the headline sample to e4m3")
@@ -288,6 +306,7 @@ def main() -> int:
         "sweep": sweep,
         "gating": gating,
         "causal": causal,
+        "head_shard_8way": head_shard,
         "fp8": fp8,
         "calibration": {"pass_ms": round(calib_ms, 3), "fit_resolve_host_ms": round(host_ms, 3),
                         "a": fit.a, "b": fit.b, "s_min": fit.s_min, "s_max": fit.s_max,

@@ -152,11 +152,12 @@ def test_determinism():
         assert torch.equal(a, b)
 
 
-def test_untouched_memory_outside_valid_rows():
+@pytest.mark.parametrize("head_dim,block", [(64, 64), (128, 128)])
+def test_untouched_memory_outside_valid_rows(head_dim, block):
     """Output rows of other heads / padding stay untouched (strided layout with a gap)."""
     import torch
     import skip_softmax_video_amd as ssa
-    cfg = VideoTokenConfig("gap", ((1, 10, 20),), num_heads=2, head_dim=64, sigma=0.5, block=64, seed=3)
+    cfg = VideoTokenConfig("gap", ((1, 10, 20),), num_heads=2, head_dim=head_dim, sigma=0.5, block=block, seed=3)
     x = make_inputs(cfg)
     T, H, D = x["q"].shape
     big = {}
@@ -165,10 +166,10 @@ def test_untouched_memory_outside_valid_rows():
         buf[:, :H] = to_device(x[n])
         big[n] = buf[:, :H]
     out_buf = torch.full((T, H + 1, D), 7.0, dtype=torch.bfloat16, device="cuda")
-    o = ssa.attn_fwd(big["q"], big["k"], big["v"], x["cu_seqlens"], 0.0, block=64, out=out_buf[:, :H])
+    o = ssa.attn_fwd(big["q"], big["k"], big["v"], x["cu_seqlens"], 0.0, block=block, out=out_buf[:, :H])
     torch.cuda.synchronize()
     assert torch.all(out_buf[:, H] == 7.0)
-    ref = osk.skip_softmax_forward(*(to_f64(x[n]) for n in ("q", "k", "v")), x["cu_seqlens"], -math.inf, 64)
+    ref = osk.skip_softmax_forward(*(to_f64(x[n]) for n in ("q", "k", "v")), x["cu_seqlens"], -math.inf, block)
     compare_outputs(o.float().cpu().numpy(), ref["o"])
 
 
