@@ -23,7 +23,8 @@
  *  - Every function returns an int status: 0 = SSA_OK, > 0 = a warning (the
  *    outputs are valid), < 0 = an error (outputs untouched unless stated).
  *    Nothing falls back silently to dense attention.
- *  - Tensors are bf16, packed "varlen": token-major [T, H, D] with T the sum
+ *  - Tensors are bf16 (q, k, v may instead be fp8 e4m3, see SSA_DTYPE_*),
+ *    packed "varlen": token-major [T, H, D] with T the sum
  *    of the B sequence lengths (the [B, S, H, D] -> varlen conversion of
  *    [TRITON] "Kernel backends"). Element (token t, head h, dim d) sits at
  *    t * stride_token + h * stride_head + d; D is contiguous. Base pointers
@@ -125,8 +126,9 @@ typedef struct ssa_thresholds {
  * P.V is computed, and the running statistics are left unchanged. Kept tiles
  * update the online softmax as in FlashAttention. The first tile is never
  * skipped. With causal = 1, Q-block i visits tiles 0..i only; keys after a
- * query are excluded from its scores, row maxima and softmax. Scores are accumulated in fp32 from bf16 inputs, P is rounded to
- * bf16 for the P.V product, O is rounded to bf16.
+ * query are excluded from its scores, row maxima and softmax. Scores are
+ * accumulated in fp32 from bf16 inputs, P is rounded to bf16 for the P.V
+ * product, O is rounded to bf16.
  *
  *  q, k, v    device, bf16 [T, H, D] (see conventions)
  *  o          device, bf16 [T, H, D], written for every valid token
