@@ -324,30 +324,57 @@ def test_causal_ragged_d128_parity(lam):
     _full_parity(RAGGED, lam, causal=True)
 
 
-def test_causal_calibration_counts():
+def _calibration_matches_forward(cfg, lams, causal):
+    """Calibration pass: dense output bit-equal to the lambda = 0 forward,
+    tiles per work-group as the oracle, counts equal to the forward's skipped
+    tiles at each lambda exactly, and to the oracle's outside the 1e-3 band."""
     import torch
     import skip_softmax_video_amd as ssa
-    cfg = RAGGED
     x, xd, cu = _inputs(cfg)
     xf = _f64(x)
-    lams = np.geomspace(1e-5, 0.7, 8)
-    o_cal, counts, tiles = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, lams, block=cfg.block, causal=True)
+    o_cal, counts, tiles = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, lams, block=cfg.block, causal=causal)
     torch.cuda.synchronize()
     counts, tiles = counts.cpu().numpy(), tiles.cpu().numpy()
     wgs = osk.workgroups(cu, cfg.num_heads, cfg.block)
-    np.testing.assert_array_equal(tiles, [i + 1 for (_, _, i) in wgs])
-    o0, _, _, _ = gpu_forward(xd, cu, 0.0, "lambda", cfg.block, mask=False, causal=True)
-    np.testing.assert_array_equal(o_cal.float().cpu().numpy(), o0)
     ts = np.log2(lams)
-    ref = osk.calibration_counts(xf["q"], xf["k"], xf["v"], cu, ts, cfg.block, causal=True)
-    d = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, -math.inf, cfg.block, fast=True, causal=True)["d"]
+    ref = osk.calibration_counts(xf["q"], xf["k"], xf["v"], cu, ts, cfg.block, causal=causal)
+    np.testing.assert_array_equal(tiles, ref["tiles"])
+    if causal:
+        np.testing.assert_array_equal(tiles, [i + 1 for (_, _, i) in wgs])
+    o0, _, _, _ = gpu_forward(xd, cu, 0.0, "lambda", cfg.block, mask=False, causal=causal)
+    np.testing.assert_array_equal(o_cal.float().cpu().numpy(), o0)
+    d = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, -math.inf, cfg.block, fast=True, causal=causal)["d"]
     for kk, lam in enumerate(lams):
-        _, _, _, mask = gpu_forward(xd, cu, lam, "lambda", cfg.block, causal=True)
+        _, _, _, mask = gpu_forward(xd, cu, lam, "lambda", cfg.block, causal=causal)
         per_wg = np.array([(mask[b, h, i] == osk.TILE_SKIPPED).sum() for (b, h, i) in wgs])
         np.testing.assert_array_equal(counts[:, kk], per_wg)
         with np.errstate(invalid="ignore"):
             band = np.array([np.sum(np.abs(d[b, h, i] - ts[kk]) <= 1e-3) for (b, h, i) in wgs])
         assert np.all(np.abs(counts[:, kk] - ref["counts"][:, kk]) <= band)
+    return counts
+
+
+def test_causal_calibration_counts():
+    _calibration_matches_forward(RAGGED, np.geomspace(1e-5, 0.7, 8), causal=True)
+
+
+def _shape_cfg(head_dim, block):
+    # two sequences, 2080 and 45 tokens: several tiles, a ragged last tile, a one-tile sequence
+    return VideoTokenConfig("shape", ((8, 13, 20), (1, 5, 9)), num_heads=2, head_dim=head_dim, sigma=0.5,
+                            block=block, seed=11)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("head_dim,block", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_calibration_all_tile_shapes(head_dim, block, causal):
+    counts = _calibration_matches_forward(_shape_cfg(head_dim, block), np.geomspace(1e-4, 1.0, 6), causal)
+    assert counts.sum() > 0
+
+
+@pytest.mark.parametrize("head_dim,block", [(64, 128), (128, 64)])
+def test_causal_other_tile_shapes(head_dim, block):
+    sk, tot, _, _ = _full_parity(_shape_cfg(head_dim, block), 1.0, causal=True)
+    assert sk.sum() > 0
 
 
 def test_causal_headline_sampled_parity():
