@@ -475,6 +475,39 @@ def test_fp8_calibration_counts_match_forward():
         np.testing.assert_array_equal(counts[:, kk], per_wg)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("head_dim,block", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_fp8_calibration_all_tile_shapes(head_dim, block, causal):
+    """e4m3 calibration pass at every tile shape: counts equal the fp8
+    forward's skipped tiles exactly and the oracle's (on the dequantized
+    inputs) outside the 1e-3 band; the output equals the lambda = 0 forward."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    cfg = _shape_cfg(head_dim, block)
+    xd, xf, scales, cu = _fp8_inputs(cfg)
+    lams = np.geomspace(1e-4, 1.0, 6)
+    o_cal, counts, tiles = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, lams, block=block, scales=scales,
+                                              causal=causal)
+    torch.cuda.synchronize()
+    counts, tiles = counts.cpu().numpy(), tiles.cpu().numpy()
+    wgs = osk.workgroups(cu, cfg.num_heads, block)
+    ts = np.log2(lams)
+    ref = osk.calibration_counts(xf["q"], xf["k"], xf["v"], cu, ts, block, causal=causal)
+    np.testing.assert_array_equal(tiles, ref["tiles"])
+    o0, _, _, _ = _fp8_forward(xd, cu, 0.0, block, scales, causal=causal, mask=False)
+    np.testing.assert_array_equal(o_cal.float().cpu().numpy(), o0)
+    d = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, -math.inf, block, fast=True, causal=causal)["d"]
+    for kk, lam in enumerate(lams):
+        _, _, _, mask = _fp8_forward(xd, cu, lam, block, scales, causal=causal)
+        per_wg = np.array([(mask[b, h, i] == osk.TILE_SKIPPED).sum() for (b, h, i) in wgs])
+        np.testing.assert_array_equal(counts[:, kk], per_wg)
+        with np.errstate(invalid="ignore"):
+            band = np.array([np.sum(np.abs(d[b, h, i] - ts[kk]) <= 1e-3) for (b, h, i) in wgs])
+        assert np.all(np.abs(counts[:, kk] - ref["counts"][:, kk]) <= band)
+    if not causal:  # causal 128-key tiles of this batch skip one tile at most (oracle)
+        assert counts.sum() > 0
+
+
 def test_fp8_headline_sampled_parity():
     """Full-size e4m3 launch at the headline shape; skip bits and outputs
     checked on sampled Q-blocks against the oracle on the dequantized inputs."""
