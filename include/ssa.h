@@ -81,7 +81,12 @@ typedef struct ssa_problem {
   int32_t dtype;             /* SSA_DTYPE_*: element type of q, k and v (o is bf16) */
   double scale_q, scale_k, scale_v; /* SSA_DTYPE_FP8_E4M3: dequantization scales,
                                 value = code * scale, each finite and > 0; ignored
-                                for bf16                                           */
+                                otherwise                                          */
+  const uint8_t* block_scale_q;      /* SSA_DTYPE_MXFP8_QK: DEVICE E8M0 scales of q,
+                                        [T, H, D / 32] bytes; ignored otherwise   */
+  const uint8_t* block_scale_k;      /* the same for k                             */
+  int64_t block_scale_stride_token;  /* bytes between tokens of both scale arrays  */
+  int64_t block_scale_stride_head;   /* bytes between heads of both scale arrays   */
 } ssa_problem;
 
 /* Element types of q, k, v. SSA_DTYPE_FP8_E4M3 is the OCP e4m3 ("e4m3fn")
@@ -93,6 +98,17 @@ typedef struct ssa_problem {
  * attention beside BF16.) */
 #define SSA_DTYPE_BF16     0
 #define SSA_DTYPE_FP8_E4M3 1
+/* SSA_DTYPE_MXFP8_QK: block-scaled ("MXFP8") q and k with bf16 v ([DOCS]
+ * "Skip Softmax Attention": skip-softmax combined with block-scaled Q/K).
+ * q and k are OCP e4m3 bytes; each run of 32 consecutive elements along D
+ * of one (token, head) row shares one E8M0 scale byte (value 2^(e - 127);
+ * e = 255 is not allowed), so value = code * scale. Q K^T runs on the fp8
+ * matrix cores with these block scales (exact products, fp32 sums), the
+ * skip test uses those fp32 scores, and v, P, P.V and o are as in bf16 mode.
+ * Element strides are shared by q, k, v, o and must be multiples of 16; the
+ * scale arrays' base pointers must be aligned to D / 32 bytes and their two
+ * strides multiples of D / 32 bytes. */
+#define SSA_DTYPE_MXFP8_QK 2
 
 /* ---- thresholds for the forward ---------------------------------------- */
 /* How the per-(sequence, head) threshold reaches the kernel ([README]

@@ -5,6 +5,9 @@ package is its thin Python binding. Build the library with
 `python -m skip_softmax_video_amd.build` (or __graft_entry__.build()).
 """
 from ._binding import (  # noqa: F401
+    DTYPE_BF16,
+    DTYPE_FP8_E4M3,
+    DTYPE_MXFP8_QK,
     EXPORTED,
     GATE_BASE,
     GATE_IGNORED,

@@ -28,6 +28,7 @@ SSA_ERR_HIP = -6
 
 DTYPE_BF16 = 0
 DTYPE_FP8_E4M3 = 1
+DTYPE_MXFP8_QK = 2
 
 THRESH_LAMBDA = 0
 THRESH_LOG2 = 1
@@ -69,6 +70,8 @@ class Problem(ctypes.Structure):
         ("stride_token", ctypes.c_int64), ("stride_head", ctypes.c_int64), ("sm_scale", ctypes.c_double),
         ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("scale_q", ctypes.c_double), ("scale_k", ctypes.c_double), ("scale_v", ctypes.c_double),
+        ("block_scale_q", ctypes.c_void_p), ("block_scale_k", ctypes.c_void_p),
+        ("block_scale_stride_token", ctypes.c_int64), ("block_scale_stride_head", ctypes.c_int64),
     ]
 
 
@@ -160,18 +163,26 @@ def _is_fp8(t) -> bool:
 
 
 def make_problem(q, cu_seqlens, block: int, sm_scale: float = 0.0, causal: bool = False,
-                 scales: Optional[Tuple[float, float, float]] = None) -> Tuple[Problem, np.ndarray]:
-    """ssa_problem for a [T, H, D] tensor (bf16, or e4m3 bytes with `scales` =
-    (scale_q, scale_k, scale_v)); returns (struct, cu array kept alive)."""
+                 scales: Optional[Tuple[float, float, float]] = None,
+                 block_scales=None) -> Tuple[Problem, np.ndarray]:
+    """ssa_problem for a [T, H, D] tensor: bf16; e4m3 bytes with per-tensor
+    `scales` = (scale_q, scale_k, scale_v); or e4m3 q/k bytes with
+    `block_scales` = (q scales, k scales), uint8 E8M0 device tensors
+    [T, H, D / 32] (MXFP8 q/k, bf16 v). Returns (struct, cu array kept alive)."""
     cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
     T, H, D = q.shape
     fp8 = _is_fp8(q)
     sq, sk, sv = scales if scales is not None else (1.0, 1.0, 1.0)
+    dtype = DTYPE_MXFP8_QK if block_scales is not None else (DTYPE_FP8_E4M3 if fp8 else DTYPE_BF16)
     prob = Problem(batch=len(cu) - 1, num_heads=H, head_dim=D, block=block,
                    cu_seqlens=cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                    stride_token=q.stride(0), stride_head=q.stride(1), sm_scale=float(sm_scale),
-                   causal=1 if causal else 0, dtype=DTYPE_FP8_E4M3 if fp8 else DTYPE_BF16,
+                   causal=1 if causal else 0, dtype=dtype,
                    scale_q=float(sq), scale_k=float(sk), scale_v=float(sv))
+    if block_scales is not None:
+        qs, ks = block_scales
+        prob.block_scale_q, prob.block_scale_k = _ptr(qs), _ptr(ks)
+        prob.block_scale_stride_token, prob.block_scale_stride_head = qs.stride(0), qs.stride(1)
     return prob, cu
 
 
@@ -186,15 +197,27 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def _check_qkv(q, k, v, o):
+def _check_qkv(q, k, v, o, block_scales=None):
     import torch
     fp8 = _is_fp8(q)
+    mx = block_scales is not None
+    if mx and not fp8:
+        raise ValueError("block_scales need e4m3 q and k (torch.float8_e4m3fn or uint8 bytes)")
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        want = torch.bfloat16 if (name == "o" or not fp8) else q.dtype
+        byte_typed = fp8 and (name in ("q", "k") or not mx) and name != "o"
+        want = q.dtype if byte_typed else torch.bfloat16
         if t.dtype != want or not t.is_cuda or t.dim() != 3:
             raise ValueError(f"{name} must be a 3-D {want} device tensor [T, H, D]")
         if t.shape != q.shape or t.stride() != q.stride():
             raise ValueError(f"{name} must match q's shape and strides")
+    if mx:
+        T, H, D = q.shape
+        qs, ks = block_scales
+        for name, t in (("q scales", qs), ("k scales", ks)):
+            if t.dtype != torch.uint8 or not t.is_cuda or tuple(t.shape) != (T, H, D // 32) or t.stride(2) != 1:
+                raise ValueError(f"{name} must be a uint8 device tensor [T, H, D / 32] with contiguous last dim")
+        if qs.stride() != ks.stride():
+            raise ValueError("q and k block scales must share strides")
 
 
 def tile_mask_dims(prob: Problem) -> Tuple[int, int]:
@@ -215,20 +238,22 @@ def calib_num_workgroups(prob: Problem) -> int:
 def attn_fwd(q, k, v, cu_seqlens, threshold: Union[float, Sequence[float]], kind: str = "lambda",
              block: int = 128, sm_scale: float = 0.0, out=None, skipped=None, total=None,
              tile_mask=None, stream=None, causal: bool = False,
-             scales: Optional[Tuple[float, float, float]] = None):
+             scales: Optional[Tuple[float, float, float]] = None, block_scales=None):
     """ssa_attn_fwd on torch tensors; returns `out` (allocated when None).
 
     threshold: one value for every head, or H values (per head); `kind` is
     "lambda", "log2" (raw) or "scale_factor" (lambda = sf / S_b).
     skipped/total: optional uint64 device tensors [B*H]; tile_mask: optional
     uint8 device tensor [B, H, nq, nk]. q, k, v may be e4m3 (torch.float8_e4m3fn
-    or uint8 bytes) with scales = (scale_q, scale_k, scale_v); out is bf16.
+    or uint8 bytes) with scales = (scale_q, scale_k, scale_v); or q, k e4m3
+    with block_scales = (q scales, k scales) [T, H, D / 32] E8M0 and v bf16
+    (MXFP8 q/k). out is bf16.
     """
     import torch
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    _check_qkv(q, k, v, out)
-    prob, cu = make_problem(q, cu_seqlens, block, sm_scale, causal, scales)
+    _check_qkv(q, k, v, out, block_scales)
+    prob, cu = make_problem(q, cu_seqlens, block, sm_scale, causal, scales, block_scales)
     vals = np.ascontiguousarray(np.atleast_1d(np.asarray(threshold, dtype=np.float64)))
     th = Thresholds(kind=_KINDS[kind], count=vals.size, values=vals.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     st = load_library().ssa_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(th),
@@ -239,13 +264,13 @@ def attn_fwd(q, k, v, cu_seqlens, threshold: Union[float, Sequence[float]], kind
 
 def attn_calibrate(q, k, v, cu_seqlens, lambdas: Sequence[float], block: int = 128, sm_scale: float = 0.0,
                    out=None, counts=None, tiles=None, stream=None, causal: bool = False,
-                   scales: Optional[Tuple[float, float, float]] = None):
+                   scales: Optional[Tuple[float, float, float]] = None, block_scales=None):
     """ssa_attn_calibrate; returns (out, counts [num_wg, n] int32, tiles [num_wg] int32) on the device."""
     import torch
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    _check_qkv(q, k, v, out)
-    prob, cu = make_problem(q, cu_seqlens, block, sm_scale, causal, scales)
+    _check_qkv(q, k, v, out, block_scales)
+    prob, cu = make_problem(q, cu_seqlens, block, sm_scale, causal, scales, block_scales)
     lam = np.ascontiguousarray(np.asarray(lambdas, dtype=np.float64))
     nwg = calib_num_workgroups(prob)
     if counts is None:

@@ -34,6 +34,7 @@ int validate_problem(const ssa_problem* p) {
     // work-groups of one sequence and tile-mask rows are indexed in int32
     if (ceil_div(s, p->block) * p->num_heads > INT32_MAX / 2) return SSA_ERR_UNSUPPORTED;
     // K/V tiles are fetched through 32-bit buffer offsets from the head's first row
+    // (bf16 V in the block-scaled mode bounds both)
     const int64_t esize = p->dtype == SSA_DTYPE_FP8_E4M3 ? 1 : 2;
     if (s > 0 && ((s - 1) * p->stride_token + p->block * p->stride_token + p->head_dim) * esize > (int64_t)UINT32_MAX)
       return SSA_ERR_UNSUPPORTED;
@@ -45,12 +46,34 @@ int validate_problem(const ssa_problem* p) {
   if (p->num_heads > 1 && p->stride_head < p->head_dim) return SSA_ERR_INVALID_ARG;
   if (!(p->sm_scale >= 0.0) || !isfinite(p->sm_scale)) return SSA_ERR_INVALID_ARG;
   if (p->causal != 0 && p->causal != 1) return SSA_ERR_INVALID_ARG;
-  if (p->dtype != SSA_DTYPE_BF16 && p->dtype != SSA_DTYPE_FP8_E4M3) return SSA_ERR_INVALID_ARG;
+  if (p->dtype != SSA_DTYPE_BF16 && p->dtype != SSA_DTYPE_FP8_E4M3 && p->dtype != SSA_DTYPE_MXFP8_QK)
+    return SSA_ERR_INVALID_ARG;
+  // 16-byte aligned e4m3 rows
+  if (p->dtype != SSA_DTYPE_BF16 && (p->stride_token % 16 != 0 || p->stride_head % 16 != 0))
+    return SSA_ERR_INVALID_ARG;
   if (p->dtype == SSA_DTYPE_FP8_E4M3) {
-    // 16-byte aligned e4m3 rows; positive finite dequantization scales
-    if (p->stride_token % 16 != 0 || p->stride_head % 16 != 0) return SSA_ERR_INVALID_ARG;
+    // positive finite dequantization scales
     for (double sc : {p->scale_q, p->scale_k, p->scale_v})
       if (!(sc > 0.0) || !isfinite(sc)) return SSA_ERR_INVALID_ARG;
+  }
+  return SSA_OK;
+}
+
+// Block-scale arrays of the MXFP8 q/k mode (forward and calibration only):
+// present, aligned to one row of scales (D / 32 bytes, read as one load),
+// strides in whole rows, and every head's rows within a 32-bit buffer range.
+int validate_block_scales(const ssa_problem* p) {
+  if (p->dtype != SSA_DTYPE_MXFP8_QK) return SSA_OK;
+  const int64_t row = p->head_dim / 32;
+  if (p->block_scale_q == nullptr || p->block_scale_k == nullptr) return SSA_ERR_INVALID_ARG;
+  if ((uintptr_t)p->block_scale_q % row != 0 || (uintptr_t)p->block_scale_k % row != 0) return SSA_ERR_INVALID_ARG;
+  const int64_t st = p->block_scale_stride_token, sh = p->block_scale_stride_head;
+  if (st < row || st % row != 0 || sh < 0 || sh % row != 0) return SSA_ERR_INVALID_ARG;
+  if (p->num_heads > 1 && sh < row) return SSA_ERR_INVALID_ARG;
+  for (int b = 0; b < p->batch; ++b) {
+    const int64_t s = (int64_t)p->cu_seqlens[b + 1] - p->cu_seqlens[b];
+    // rows up to the end of the last tile are addressed (and read as zero past S)
+    if (s > 0 && (s + p->block) * st > (int64_t)UINT32_MAX) return SSA_ERR_UNSUPPORTED;
   }
   return SSA_OK;
 }
@@ -148,6 +171,13 @@ ssa::LaunchParams base_params(const ssa_problem* p, const void* q, const void* k
   lp.causal = p->causal;
   lp.fp8 = fp8 ? 1 : 0;
   lp.v_scale = fp8 ? (float)p->scale_v : 1.0f;
+  if (p->dtype == SSA_DTYPE_MXFP8_QK) {  // the block scales are applied inside the MFMA
+    lp.mxqk = 1;
+    lp.q_bscale = p->block_scale_q;
+    lp.k_bscale = p->block_scale_k;
+    lp.bs_tok = p->block_scale_stride_token;
+    lp.bs_head = p->block_scale_stride_head;
+  }
   return lp;
 }
 
@@ -202,6 +232,8 @@ int ssa_attn_fwd(const ssa_problem* p, const void* q, const void* k, const void*
   if (st != SSA_OK) return st;
   st = validate_tensors(q, k, v, o);
   if (st != SSA_OK) return st;
+  st = validate_block_scales(p);
+  if (st != SSA_OK) return st;
   if (th == nullptr || th->values == nullptr) return SSA_ERR_INVALID_ARG;
   if (th->count != 1 && th->count != p->num_heads) return SSA_ERR_INVALID_ARG;
   const int B = p->batch, H = p->num_heads;
@@ -242,6 +274,8 @@ int ssa_attn_calibrate(const ssa_problem* p, const void* q, const void* k, const
   int st = validate_problem(p);
   if (st != SSA_OK) return st;
   st = validate_tensors(q, k, v, o);
+  if (st != SSA_OK) return st;
+  st = validate_block_scales(p);
   if (st != SSA_OK) return st;
   if (lambdas == nullptr || counts == nullptr || tiles == nullptr) return SSA_ERR_INVALID_ARG;
   if (n < 1 || n > ssa::kMaxCalib) return SSA_ERR_INVALID_ARG;

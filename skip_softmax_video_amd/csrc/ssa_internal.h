@@ -26,6 +26,10 @@ struct LaunchParams {
   int32_t causal;                            // 1: Q-block i visits KV tiles 0..i, keys after the query masked
   int32_t fp8;                               // 1: q, k, v are e4m3 bytes (o stays bf16)
   float v_scale;                             // fp8: dequantization scale of v (1 for bf16)
+  int32_t mxqk;                              // 1: q, k are e4m3 bytes with E8M0 block scales (v bf16)
+  const uint8_t* q_bscale;                   // mxqk: [T, H, D / 32] scales of q and k
+  const uint8_t* k_bscale;
+  int64_t bs_tok, bs_head;                   // mxqk: byte strides of the scale arrays
   int32_t nseq;                              // sequences in this launch
   int32_t total_wg;                          // work-groups in this launch
   int32_t seq_abs0;                          // batch index of the first sequence

@@ -750,6 +750,275 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_fp8(const LaunchParams 
   }
 }
 
+// ===========================================================================
+// Block-scaled q/k (MXFP8) variant: S^T = K Q^T on the fp8 matrix cores with
+// one E8M0 scale per 32 consecutive d of every q and k row; v is bf16, and
+// the skip vote, softmax, P and O^T += V^T P^T are those of the bf16 kernel.
+// In v_mfma_scale_f32_32x32x64_f8f6f4 lane l holds row l % 32 of each
+// operand; its bytes 0-15 are reduction indices 16 (l / 32) .. +15 and its
+// bytes 16-31 are 32 + 16 (l / 32) .. +15, and the scale of reduction block
+// 0 (indices 0-31) is supplied by lane l % 32, that of block 1 by lane
+// l % 32 + 32 (measured on gfx950). So for the 64-wide d step s a lane
+// gathers d [64 s + 16 h, +16) and [64 s + 32 + 16 h, +16) (h = l / 32) and
+// supplies the scale of MX block 2 s + h. A scale row (D / 32 bytes of one
+// token and head) is fetched with one buffer load; rows past the sequence end
+// read as zero.
+// ===========================================================================
+// A operand of the block-scaled S^T = K Q^T: key 32 kb + l32, d granules
+// 4 s + hl and 4 s + 2 + hl (16 bytes each), in the order the scales need.
+template <class SH>
+__device__ __forceinline__ intx8 read_k8_mx(const uint8_t* k_lds, int kb, int s, int l32, int hl) {
+  const int row = 32 * kb + l32;
+  const int sw = swz_k8<SH::CH>(row);
+  const uint4 a = *reinterpret_cast<const uint4*>(k_lds + (row * SH::CH + ((4 * s + hl) ^ sw)) * 16);
+  const uint4 b = *reinterpret_cast<const uint4*>(k_lds + (row * SH::CH + ((4 * s + 2 + hl) ^ sw)) * 16);
+  return intx8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+// Scale row at byte voff (per lane) + soff (uniform); the range check covers
+// both, so rows at or past the sequence end read as zero.
+template <int D>
+__device__ __forceinline__ uint32_t load_scale_row(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff) {
+  if constexpr (D == 128) {
+    return __builtin_amdgcn_raw_buffer_load_b32(rsrc, (int)voff, (int)soff, 0);
+  } else {
+    return __builtin_amdgcn_raw_buffer_load_b16(rsrc, (int)voff, (int)soff, 0);
+  }
+}
+
+template <int D, int BLK, bool CALIB>
+__global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_mxqk(const LaunchParams p) {
+  using SH = Shape<D, BLK>;   // bf16 V tile, softmax, P.V
+  using S8 = Shape8<D, BLK>;  // e4m3 K tile, S^T
+  constexpr int SROW = D / 32;  // scale bytes per row
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[BLK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[BLK * D];
+  __shared__ uint64_t vote[SH::NW];
+  __shared__ float dvote[SH::NW];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  const int G = p.total_wg;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int L = xcd * (G >> 3) + min(xcd, G & 7) + (bid >> 3);
+  int b = 0;
+  while (b + 1 < p.nseq && p.wg_start[b + 1] <= L) ++b;
+  const int tok0 = p.tok_start[b];
+  const int S = p.tok_start[b + 1] - tok0;
+  const int nQ = (S + BLK - 1) / BLK;
+  const int rem = L - p.wg_start[b];
+  const int h = rem / nQ;
+  const int qb = p.causal ? nQ - 1 - (rem - h * nQ) : rem - h * nQ;
+  const int nK = p.causal ? qb + 1 : nQ;
+  const int row = p.wg_start[b] + h * nQ + qb;
+  const int H = p.num_heads;
+  const int64_t head_off = (int64_t)tok0 * p.stride_tok + (int64_t)h * p.stride_head;  // elements
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) + head_off;
+  const uint16_t* vbase = p.v + head_off;
+  const uint32_t k_bytes = head_extent8<D>(S, p.stride_tok);
+  const uint32_t v_bytes = head_extent<D>(S, p.stride_tok);
+  const int64_t sc_off = (int64_t)tok0 * p.bs_tok + (int64_t)h * p.bs_head;
+  const uint32_t sc_bytes = S > 0 ? (uint32_t)((int64_t)(S - 1) * p.bs_tok + SROW) : 0u;
+  const __amdgpu_buffer_rsrc_t ks_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_bscale + sc_off), 0, sc_bytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t qs_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.q_bscale + sc_off), 0, sc_bytes, kBufferFlags);
+
+  // K tile 0 and the scale rows of its keys (lane: key 32 kb + l32; the
+  // host keeps (S + BLK) * bs_tok within 32 bits)
+  const uint32_t sc_lane = (uint32_t)(l32 * p.bs_tok);
+  const uint32_t sc_blk = (uint32_t)(32 * p.bs_tok);  // one 32-key block
+  dma_load8<D, BLK, false>(kbase, k_bytes, k_lds, 0, p.stride_tok, wave, lane);
+  uint32_t ks[S8::KB];
+#pragma unroll
+  for (int kb = 0; kb < S8::KB; ++kb) ks[kb] = load_scale_row<D>(ks_rsrc, sc_lane, kb * sc_blk);
+
+  // Q fragment (B operand): query qrow, d bytes [64 s + 16 hl, +16) and
+  // [64 s + 32 + 16 hl, +16), and the scale of its MX block 2 s + hl
+  const int qrow = qb * BLK + wave * 32 + l32;
+  const bool qvalid = qrow < S;
+  intx8 qf[S8::DS];
+  uint32_t qsc[S8::DS];
+  {
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + head_off + (int64_t)(qvalid ? qrow : 0) * p.stride_tok +
+                        16 * hl;
+#pragma unroll
+    for (int s = 0; s < S8::DS; ++s) {
+      uint4 a = make_uint4(0u, 0u, 0u, 0u), c = make_uint4(0u, 0u, 0u, 0u);
+      if (qvalid) {
+        a = *reinterpret_cast<const uint4*>(qp + 64 * s);
+        c = *reinterpret_cast<const uint4*>(qp + 64 * s + 32);
+      }
+      qf[s] = intx8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z, (int)c.w};
+    }
+    const uint32_t qs = load_scale_row<D>(qs_rsrc, sc_lane, (uint32_t)((qb * BLK + wave * 32) * p.bs_tok));
+#pragma unroll
+    for (int s = 0; s < S8::DS; ++s) qsc[s] = qs >> (8 * (2 * s + hl));  // byte 0: this lane's block
+  }
+
+  const float c2 = p.scale_log2;
+  const float t = CALIB ? 0.0f : p.t_bh[b * H + h];
+  const int ncal = CALIB ? p.ncal : 0;
+  const float my_t = (CALIB && lane < ncal) ? p.cal_t[lane] : INFINITY;
+  int ncount = 0;
+  float m_true = -INFINITY, m_use = -INFINITY, l = 0.0f;
+  floatx16 acc[SH::MB];
+#pragma unroll
+  for (int mb = 0; mb < SH::MB; ++mb) acc[mb] = floatx16{};
+  int skipped = 0;
+  const int tr_row = 4 * hl + ((lane & 15) >> 2);
+  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int tr_elem = 4 * (lane & 1);
+
+  wait_dma();
+  __syncthreads();
+
+  for (int j = 0; j < nK; ++j) {
+    const int nvalid = min(BLK, S - j * BLK);
+
+    // ---- S^T = K_j Q^T with the block scales (always paid) ---------------
+    floatx16 sc[SH::KB];
+#pragma unroll
+    for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
+#pragma unroll
+    for (int s = 0; s < S8::DS; ++s) {
+      intx8 ka[S8::KB];
+#pragma unroll
+      for (int kb = 0; kb < S8::KB; ++kb) ka[kb] = read_k8_mx<S8>(k_lds, kb, s, l32, hl);
+#pragma unroll
+      for (int kb = 0; kb < S8::KB; ++kb)
+        sc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[kb], qf[s], sc[kb], 0, 0, 0,
+                                                                 (int)(ks[kb] >> (8 * (2 * s + hl))), 0, (int)qsc[s]);
+    }
+    const int kmax = (p.causal && j == qb) ? min(nvalid, wave * 32 + l32 + 1) : nvalid;
+    if (p.causal ? j == qb : nvalid < BLK) {
+#pragma unroll
+      for (int kb = 0; kb < SH::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (key >= kmax) sc[kb][r] = -INFINITY;
+        }
+    }
+
+    // ---- tile row max and the skip vote ----------------------------------
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < SH::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    float rowmax, x;
+    tile_margin(xhalf_max(mx), c2, m_true, rowmax, x);
+    if (!qvalid) x = -INFINITY;
+    if constexpr (CALIB) {
+      const float dw = wave_max(x);
+      if (lane == 0) dvote[wave] = dw;
+    } else {
+      const bool kw = wave_any(x >= t);
+      if (lane == 0) vote[wave] = kw ? 1ull : 0ull;
+    }
+    __syncthreads();  // votes visible; every wave is done reading K_j and V_{j-1}
+
+    bool keep;
+    if constexpr (CALIB) {
+      float d = dvote[0];
+#pragma unroll
+      for (int w = 1; w < SH::NW; ++w) d = fmaxf(d, dvote[w]);
+      ncount += d < my_t ? 1 : 0;
+      keep = true;
+    } else {
+      uint64_t all = vote[0];
+#pragma unroll
+      for (int w = 1; w < SH::NW; ++w) all |= vote[w];
+      keep = __builtin_amdgcn_readfirstlane(all != 0 ? 1 : 0) != 0;
+      skipped += keep ? 0 : 1;
+      if (p.tile_mask != nullptr && tid == 0)
+        p.tile_mask[((int64_t)((p.seq_abs0 + b) * H + h) * p.mask_nq + qb) * p.mask_nk + j] = keep ? 0 : 1;
+    }
+
+    if (j + 1 < nK) {
+      dma_load8<D, BLK, false>(kbase, k_bytes, k_lds, (j + 1) * BLK, p.stride_tok, wave, lane);
+#pragma unroll
+      for (int kb = 0; kb < S8::KB; ++kb)
+        ks[kb] = load_scale_row<D>(ks_rsrc, sc_lane, (uint32_t)((j + 1) * BLK * p.bs_tok) + kb * sc_blk);
+    }
+    bf16x8 pb[SH::KS];
+    if (keep) {
+      dma_load<D, BLK, true>(vbase, v_bytes, v_lds, j * BLK, p.stride_tok, wave, lane);
+      m_true = fmaxf(m_true, rowmax);
+      if (wave_any(rowmax > m_use + kRescaleSlack)) {
+        const float m_new = fmaxf(m_use, rowmax);
+        const float alpha = fast_exp2(m_use - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < SH::MB; ++mb) acc[mb] *= alpha;
+        m_use = m_new;
+      }
+      const float nm = -m_use;
+#pragma unroll
+      for (int s = 0; s < SH::KS; ++s) {
+        floatx8 e;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          e[r] = fast_exp2(fmaf(sc[s >> 1][8 * (s & 1) + r], c2, nm));
+          l += e[r];
+        }
+        pb[s] = __builtin_convertvector(e, bf16x8);
+      }
+    }
+    wait_dma();
+    __syncthreads();  // K_{j+1}, its scales and V_j visible
+
+    if (keep) {
+      bf16x8 va[3][SH::MB];
+#pragma unroll
+      for (int s = 0; s < 2 && s < SH::KS; ++s)
+#pragma unroll
+        for (int mb = 0; mb < SH::MB; ++mb) va[s][mb] = read_vt<SH>(v_lds, s, mb, tr_row, tr_chunk, tr_elem);
+#pragma unroll
+      for (int s = 0; s < SH::KS; ++s) {
+        if (s + 2 < SH::KS) {
+#pragma unroll
+          for (int mb = 0; mb < SH::MB; ++mb)
+            va[(s + 2) % 3][mb] = read_vt<SH>(v_lds, s + 2, mb, tr_row, tr_chunk, tr_elem);
+        }
+#pragma unroll
+        for (int mb = 0; mb < SH::MB; ++mb)
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s % 3][mb], pb[s], acc[mb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  const float inv = 1.0f / xhalf_sum(l);
+  if (qvalid) {
+    uint16_t* op = p.o + head_off + (int64_t)qrow * p.stride_tok;
+#pragma unroll
+    for (int mb = 0; mb < SH::MB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const floatx4 f = {acc[mb][4 * g] * inv, acc[mb][4 * g + 1] * inv, acc[mb][4 * g + 2] * inv,
+                           acc[mb][4 * g + 3] * inv};
+        const bf16x4 o4 = __builtin_convertvector(f, bf16x4);
+        *reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * g + 4 * hl) = o4;
+      }
+  }
+  if constexpr (CALIB) {
+    if (wave == 0 && lane < ncal) p.counts[(p.wg_abs0 + row) * ncal + lane] = ncount;
+    if (tid == 0) p.tiles[p.wg_abs0 + row] = nK;
+  } else {
+    if (tid == 0) {
+      const int64_t bh = (int64_t)(p.seq_abs0 + b) * H + h;
+      if (p.skipped_bh != nullptr) atomicAdd((unsigned long long*)&p.skipped_bh[bh], (unsigned long long)skipped);
+      if (p.total_bh != nullptr) atomicAdd((unsigned long long*)&p.total_bh[bh], (unsigned long long)nK);
+    }
+  }
+}
+
 __global__ void fill_u8_kernel(uint8_t* dst, int64_t n, uint8_t value) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     dst[i] = value;
@@ -765,6 +1034,9 @@ int launch(const LaunchParams& p, hipStream_t stream) {
   if (p.fp8) {
     using SH = Shape8<D, BLK>;
     hipLaunchKernelGGL((fwd_kernel_fp8<D, BLK, CALIB>), dim3(p.total_wg), dim3(SH::NT), 0, stream, p);
+  } else if (p.mxqk) {
+    using SH = Shape<D, BLK>;
+    hipLaunchKernelGGL((fwd_kernel_mxqk<D, BLK, CALIB>), dim3(p.total_wg), dim3(SH::NT), 0, stream, p);
   } else {
     using SH = Shape<D, BLK>;
     hipLaunchKernelGGL((fwd_kernel<D, BLK, CALIB>), dim3(p.total_wg), dim3(SH::NT), 0, stream, p);

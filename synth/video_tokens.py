@@ -155,6 +155,82 @@ def make_fp8_inputs(x: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
     return out
 
 
+# MXFP8 (OCP microscaling formats, MX E4M3): one E8M0 scale per block of
+# MX_BLOCK consecutive elements along the head dimension.
+MX_BLOCK = 32
+E4M3_EMAX = 8  # exponent of the largest e4m3 normal: 448 = 1.75 * 2^8
+
+
+def e8m0_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Value of E8M0 scale bytes: 2^(code - 127) (code 255, NaN, is never produced here)."""
+    return np.ldexp(1.0, np.asarray(codes, dtype=np.int32) - 127)
+
+
+_BF16_TO_E4M3 = None
+
+
+def _bf16_to_e4m3_table() -> np.ndarray:
+    """e4m3 code (round to nearest even, saturating) of every finite bf16 bit pattern."""
+    global _BF16_TO_E4M3
+    if _BF16_TO_E4M3 is None:
+        with np.errstate(invalid="ignore"):
+            v = bf16_bits_to_f32(np.arange(65536, dtype=np.uint32).astype(np.uint16)).astype(np.float64)
+        _BF16_TO_E4M3 = f32_to_e4m3_bits(np.where(np.isfinite(v), v, 0.0))
+    return _BF16_TO_E4M3
+
+
+def quantize_mxfp8_bf16(bits: np.ndarray):
+    """MX E4M3 quantization of bf16 bit patterns [..., D] along the last axis.
+
+    Each block of 32 consecutive elements gets the shared scale
+    X = 2^(floor(log2(amax)) - 8) (E8M0 code floor(log2(amax)) + 119, at
+    least 0), and each element the e4m3 code of v / X, rounded to nearest
+    even and saturated at +-448. Because X is a power of two, v / X is the
+    bf16 value with its exponent field lowered by log2(X), so the code of a
+    normal v comes from the bf16 -> e4m3 table; a scaled magnitude below the
+    bf16 normal range gives +-0, zeros stay +-0, and bf16 subnormals are
+    rounded directly. Returns (codes uint8 [..., D], scales uint8 [..., D / 32])."""
+    b = np.asarray(bits, dtype=np.uint16)
+    D = b.shape[-1]
+    assert D % MX_BLOCK == 0
+    lut = _bf16_to_e4m3_table()
+    blk = b.reshape(b.shape[:-1] + (D // MX_BLOCK, MX_BLOCK)).astype(np.int32)
+    field = (blk & 0x7FFF) >> 7                      # bf16 exponent field of each element
+    amax_field = field.max(axis=-1)                  # that of the block maximum
+    scale = np.clip(amax_field - E4M3_EMAX, 0, 254)  # E8M0 code: (amax_field - 127) - 8 + 127
+    e = (scale - 127)[..., None]                     # X = 2^e
+    ok = (field >= 1) & ((field - e) >= 1)           # a normal v whose v / X is still a bf16 normal
+    shifted = (blk - (e << 7)) & 0xFFFF
+    codes = np.where(ok, lut[shifted], np.where(blk & 0x8000, 0x80, 0)).astype(np.uint8)
+    sub = (field == 0) & ((blk & 0x7F) != 0)         # bf16 subnormals: round v / X directly
+    if np.any(sub):
+        v = bf16_bits_to_f32(blk[sub].astype(np.uint16)).astype(np.float64)
+        codes[sub] = f32_to_e4m3_bits(v / np.ldexp(1.0, np.broadcast_to(e, blk.shape)[sub]))
+    return codes.reshape(b.shape), scale.astype(np.uint8)
+
+
+def mxfp8_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Exact fp64 values code * 2^(scale - 127) of MX E4M3 data [..., D]."""
+    return e4m3_bits_to_f32(codes).astype(np.float64) * np.repeat(e8m0_to_f64(scales), MX_BLOCK, axis=-1)
+
+
+def make_mxfp8_qk_inputs(x: Dict[str, np.ndarray], chunk: int = 4096) -> Dict[str, np.ndarray]:
+    """MX E4M3 versions of q and k from `make_inputs` (v stays bf16):
+    q8, k8 uint8 [T, H, D] and q_bscale, k_bscale uint8 [T, H, D / 32].
+    Tokens are processed `chunk` at a time to bound host memory."""
+    out = {"cu_seqlens": x["cu_seqlens"], "v": x["v"]}
+    for n in ("q", "k"):
+        src = np.asarray(x[n])
+        T, H, D = src.shape
+        codes = np.empty((T, H, D), dtype=np.uint8)
+        scales = np.empty((T, H, D // MX_BLOCK), dtype=np.uint8)
+        for t0 in range(0, T, chunk):
+            codes[t0:t0 + chunk], scales[t0:t0 + chunk] = quantize_mxfp8_bf16(src[t0:t0 + chunk])
+        out[n + "8"] = codes
+        out[n + "_bscale"] = scales
+    return out
+
+
 def grid_positions(grid: Sequence[int]) -> np.ndarray:
     """(S, 3) float64 grid coordinates (f, r, c) in frame-major token order."""
     f, h, w = grid

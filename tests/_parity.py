@@ -36,8 +36,10 @@ def to_f64(bits: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def gpu_forward(xd: Dict, cu, threshold, kind: str, block: int, mask: bool = True, causal: bool = False):
-    """Run ssa_attn_fwd; return (o fp32 numpy [T,H,D], skipped [B,H], total [B,H], mask or None)."""
+def gpu_forward(xd: Dict, cu, threshold, kind: str, block: int, mask: bool = True, causal: bool = False,
+                block_scales=None):
+    """Run ssa_attn_fwd; return (o fp32 numpy [T,H,D], skipped [B,H], total [B,H], mask or None).
+    `block_scales` = (q scales, k scales) selects block-scaled e4m3 q/k."""
     import torch
     import skip_softmax_video_amd as ssa
     B = len(cu) - 1
@@ -50,7 +52,7 @@ def gpu_forward(xd: Dict, cu, threshold, kind: str, block: int, mask: bool = Tru
         nq, nk = ssa.tile_mask_dims(prob)
         tm = torch.empty((B, H, nq, nk), dtype=torch.uint8, device="cuda")
     o = ssa.attn_fwd(xd["q"], xd["k"], xd["v"], cu, threshold, kind=kind, block=block,
-                     skipped=skipped, total=total, tile_mask=tm, causal=causal)
+                     skipped=skipped, total=total, tile_mask=tm, causal=causal, block_scales=block_scales)
     torch.cuda.synchronize()
     return (o.float().cpu().numpy(), skipped.cpu().numpy().reshape(B, H), total.cpu().numpy().reshape(B, H),
             None if tm is None else tm.cpu().numpy())

@@ -627,3 +627,117 @@ def test_headline_calibration_counts_equal_forward_skips(fp8):
         assert int(total.sum()) == int(tiles.sum())
     log(f"  fp8={fp8}: calibration counts equal forward skips at 5 of 16 thresholds "
         f"(sparsity {per_lam[0] / int(tiles.sum()):.3f} .. {per_lam[-1] / int(tiles.sum()):.3f})")
+
+
+# ---- block-scaled (MXFP8) q/k with bf16 v ------------------------------------------------------
+def _mx_inputs(cfg):
+    """Device tensors (e4m3 q/k bytes, E8M0 block scales, bf16 v) and the
+    oracle's fp64 inputs: q/k dequantized exactly, v as bf16."""
+    import torch
+    from synth import make_mxfp8_qk_inputs, mxfp8_dequantize
+    x = make_inputs(cfg)
+    m = make_mxfp8_qk_inputs(x)
+    xd = {"q": torch.from_numpy(m["q8"]).cuda(), "k": torch.from_numpy(m["k8"]).cuda(), "v": to_device(x["v"])}
+    bs = (torch.from_numpy(m["q_bscale"]).cuda(), torch.from_numpy(m["k_bscale"]).cuda())
+    xf = {"q": mxfp8_dequantize(m["q8"], m["q_bscale"]), "k": mxfp8_dequantize(m["k8"], m["k_bscale"]),
+          "v": to_f64(x["v"])}
+    return xd, bs, xf, x["cu_seqlens"]
+
+
+def _mx_full_parity(cfg, lam, causal=False):
+    xd, bs, xf, cu = _mx_inputs(cfg)
+    H, blk = cfg.num_heads, cfg.block
+    log(f"[{cfg.name} mxfp8 q/k] D={cfg.head_dim} block={blk} lambda={lam} causal={causal}")
+    o, sk, tot, mask = gpu_forward(xd, cu, lam, "lambda", blk, causal=causal, block_scales=bs)
+    t = t_matrix(cu, H, lam, "lambda")
+    ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk, causal=causal)
+    band, mism = compare_masks(mask, ref, t, osk.workgroups(cu, H, blk))
+    forced = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk, forced_mask=mask, causal=causal)
+    mx, mean = compare_outputs(o, forced["o"])
+    np.testing.assert_array_equal(sk, (mask == osk.TILE_SKIPPED).sum(axis=(2, 3)))
+    np.testing.assert_array_equal(tot, ref["total"])
+    log(f"  skipped {sk.sum()}/{tot.sum()} band {band} band-mismatch {mism} max-abs {mx:.2e} mean-abs {mean:.2e}")
+    return sk, tot
+
+
+@pytest.mark.parametrize("lam", [0.0, 1e-2, 1.0])
+def test_mx_tiny_parity(lam):
+    sk, _ = _mx_full_parity(CONFIGS["tiny"], lam)
+    assert (sk.sum() == 0) == (lam == 0.0)
+
+
+@pytest.mark.parametrize("lam,causal", [(0.0, False), (1e-2, False), (1e-2, True)])
+def test_mx_ragged_d128_parity(lam, causal):
+    _mx_full_parity(RAGGED, lam, causal=causal)
+
+
+@pytest.mark.parametrize("head_dim,block", [(64, 128), (128, 64)])
+def test_mx_other_tile_shapes(head_dim, block):
+    sk, _ = _mx_full_parity(_shape_cfg(head_dim, block), 1e-1)
+    assert sk.sum() > 0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("head_dim,block", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_mx_calibration_all_tile_shapes(head_dim, block, causal):
+    """Counts equal the block-scaled forward's skipped tiles exactly and the
+    oracle's outside the 1e-3 band; the output equals the lambda = 0 forward."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    cfg = _shape_cfg(head_dim, block)
+    xd, bs, xf, cu = _mx_inputs(cfg)
+    lams = np.geomspace(1e-4, 1.0, 6)
+    o_cal, counts, tiles = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, lams, block=block, causal=causal,
+                                              block_scales=bs)
+    torch.cuda.synchronize()
+    counts, tiles = counts.cpu().numpy(), tiles.cpu().numpy()
+    wgs = osk.workgroups(cu, cfg.num_heads, block)
+    ts = np.log2(lams)
+    ref = osk.calibration_counts(xf["q"], xf["k"], xf["v"], cu, ts, block, causal=causal)
+    np.testing.assert_array_equal(tiles, ref["tiles"])
+    o0, _, _, _ = gpu_forward(xd, cu, 0.0, "lambda", block, mask=False, causal=causal, block_scales=bs)
+    np.testing.assert_array_equal(o_cal.float().cpu().numpy(), o0)
+    d = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, -math.inf, block, fast=True, causal=causal)["d"]
+    for kk, lam in enumerate(lams):
+        _, _, _, mask = gpu_forward(xd, cu, lam, "lambda", block, causal=causal, block_scales=bs)
+        per_wg = np.array([(mask[b, h, i] == osk.TILE_SKIPPED).sum() for (b, h, i) in wgs])
+        np.testing.assert_array_equal(counts[:, kk], per_wg)
+        with np.errstate(invalid="ignore"):
+            band = np.array([np.sum(np.abs(d[b, h, i] - ts[kk]) <= 1e-3) for (b, h, i) in wgs])
+        assert np.all(np.abs(counts[:, kk] - ref["counts"][:, kk]) <= band)
+    if not causal:
+        assert counts.sum() > 0
+
+
+def test_mx_headline_sampled_parity():
+    """Full-size block-scaled q/k launch at the headline shape: skip bits and
+    outputs on sampled Q-blocks against the oracle on the dequantized q/k."""
+    cfg = CONFIGS["headline"]
+    xd, bs, xf, cu = _mx_inputs(cfg)
+    H, blk = cfg.num_heads, cfg.block
+    scale = osk.default_sm_scale(cfg.head_dim)
+    qbs = sample_qblocks(cu, H, blk, [0, 39], 3, seed=cfg.seed)
+    S = int(cu[1])
+    for lam in (0.0, 8e-3):
+        log(f"[headline mxfp8 q/k] lambda={lam}: GPU forward (full launch)")
+        o, sk, tot, mask = gpu_forward(xd, cu, lam, "lambda", blk, block_scales=bs)
+        t = t_matrix(cu, H, lam, "lambda")
+        assert np.all(tot == osk.n_tiles(S, blk) ** 2)
+        worst, sum_abs, n_abs = 0.0, 0.0, 0
+        for (b, h, i) in qbs:
+            kh, vh = xf["k"][:, h], xf["v"][:, h]
+            r0, r1 = i * blk, min(S, (i + 1) * blk)
+            qh = xf["q"][r0:r1, h]
+            d, _ = osk.tile_stats_fast(qh, kh, blk, scale)
+            near = np.abs(d - t[b, h]) <= 1e-3
+            gpu_skip = mask[b, h, i] == osk.TILE_SKIPPED
+            assert not np.any((gpu_skip != (d < t[b, h])) & ~near), f"skip mismatch at {(b, h, i)}"
+            ref = osk.skip_softmax_qblock(qh, kh, vh, t[b, h], blk, scale, forced_skip=gpu_skip)
+            diff = np.abs(o[r0:r1, h] - ref["o"])
+            worst = max(worst, float(diff.max()))
+            sum_abs += float(diff.sum())
+            n_abs += diff.size
+        assert worst <= 2e-2 and sum_abs / n_abs <= 2e-3, f"output mismatch {worst:.3e} {sum_abs / n_abs:.3e}"
+        log(f"  sparsity {sk.sum() / tot.sum():.4f} max-abs {worst:.2e} mean-abs {sum_abs / n_abs:.2e}")
+        if lam > 0:
+            assert sk.sum() > 0

@@ -127,7 +127,22 @@ FAKE = 1 << 20  # aligned, never dereferenced: validation fails first
     (dict(stride_token=100), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
     (dict(sm_scale=-1.0), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
     (dict(causal=2), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(dtype=3), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),           # unknown element type
+    # block-scaled (MXFP8) q/k: the scale arrays are required, aligned to a row
+    # of D / 32 bytes, strided in whole rows and addressable in 32 bits
     (dict(dtype=2), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(dtype=2, block_scale_q=FAKE, block_scale_k=FAKE + 1, block_scale_stride_token=8,
+          block_scale_stride_head=4), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(dtype=2, block_scale_q=FAKE, block_scale_k=FAKE, block_scale_stride_token=6,
+          block_scale_stride_head=4), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(dtype=2, block_scale_q=FAKE, block_scale_k=FAKE, block_scale_stride_token=8,
+          block_scale_stride_head=0), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),   # two heads on one row
+    (dict(dtype=2, block_scale_q=FAKE, block_scale_k=FAKE, block_scale_stride_token=8,
+          block_scale_stride_head=4, stride_token=264, stride_head=136), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(dtype=2, block_scale_q=FAKE, block_scale_k=FAKE, block_scale_stride_token=1 << 30,
+          block_scale_stride_head=4), (0, [0.1]), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(dtype=2, block_scale_q=FAKE, block_scale_k=FAKE, block_scale_stride_token=8,
+          block_scale_stride_head=4), (0, [1.5]), ssa.SSA_ERR_THRESHOLD_RANGE),  # scales fine, lambda not
     (dict(dtype=1, scale_q=1.0, scale_k=1.0, scale_v=0.0), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
     (dict(dtype=1, scale_q=1.0, scale_k=float("inf"), scale_v=1.0), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
     (dict(dtype=1, scale_q=1.0, scale_k=1.0, scale_v=1.0, stride_token=264, stride_head=136),
