@@ -277,12 +277,35 @@ def main() -> int:
     log(f"fp8: dense {f_dense_ms:.2f} ms, lambda {lam07:.4g} -> {f_ms:.2f} ms (sparsity {f_sp:.4f})")
     del d8
 
+    # block-scaled (MXFP8) q/k with bf16 v: E8M0 scales over 32 consecutive d
+    from synth import make_mxfp8_qk_inputs
+    log("quantizing the headline q/k to MX e4m3 (one E8M0 scale per 32 d)")
+    mxi = make_mxfp8_qk_inputs(x)
+    dm = {n: torch.from_numpy(mxi[n + "8"]).cuda() for n in ("q", "k")}
+    bsc = (torch.from_numpy(mxi["q_bscale"]).cuda(), torch.from_numpy(mxi["k_bscale"]).cuda())
+    del mxi
+    mx_fwd = lambda lam: (lambda: ssa.attn_fwd(dm["q"], dm["k"], dx["v"], cu, lam, block=blk, out=o,
+                                               block_scales=bsc))
+    ssa.attn_fwd(dm["q"], dm["k"], dx["v"], cu, lam07, block=blk, out=o, skipped=skipped, total=total,
+                 block_scales=bsc)
+    torch.cuda.synchronize()
+    m_sp = float(skipped.sum()) / float(total.sum())
+    m_dense_ms = time_launches(mx_fwd(0.0), args.warmup, args.steps)
+    m_ms = time_launches(mx_fwd(lam07), args.warmup, args.steps)
+    block_scaled = {"achieved_tile_sparsity": round(m_sp, 4), "dense_ms": round(m_dense_ms, 3), "ms": round(m_ms, 3),
+                    "speedup_vs_dense": round(m_dense_ms / m_ms, 3),
+                    "dense_tflops": round(cfg.dense_flops() / (m_dense_ms * 1e-3) / 1e12, 2),
+                    "tflops_dense_equiv": round(cfg.dense_flops() / (m_ms * 1e-3) / 1e12, 2)}
+    log(f"mxfp8 q/k: dense {m_dense_ms:.2f} ms, lambda {lam07:.4g} -> {m_ms:.2f} ms (sparsity {m_sp:.4f})")
+    del dm, bsc
+
     dense_flops = cfg.dense_flops()
     exec_flops = dense_flops / 2 * (2 - s_ach)
     value = dense_flops / (sparse_ms * 1e-3) / 1e12
     dense_tf = dense_flops / (dense_ms * 1e-3) / 1e12
     exec_tf = exec_flops / (sparse_ms * 1e-3) / 1e12
     fp8["speedup_vs_bf16_same_lambda"] = round(sparse_ms / fp8["ms"], 3)
+    block_scaled["speedup_vs_bf16_same_lambda"] = round(sparse_ms / block_scaled["ms"], 3)
     result = {
         "metric": "skip-softmax attn TFLOPS (dense-equiv) + speedup vs dense @S=75,600 H=40 D=128",
         "value": round(value, 2),
@@ -308,6 +331,7 @@ def main() -> int:
         "causal": causal,
         "head_shard_8way": head_shard,
         "fp8": fp8,
+        "mxfp8_qk_bf16_v": block_scaled,
         "calibration": {"pass_ms": round(calib_ms, 3), "fit_resolve_host_ms": round(host_ms, 3),
                         "a": fit.a, "b": fit.b, "s_min": fit.s_min, "s_max": fit.s_max,
                         "n_used": fit.n_used, "resolved": resolved,
