@@ -741,3 +741,32 @@ def test_mx_headline_sampled_parity():
         log(f"  sparsity {sk.sum() / tot.sum():.4f} max-abs {worst:.2e} mean-abs {sum_abs / n_abs:.2e}")
         if lam > 0:
             assert sk.sum() > 0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mx_strided_layout_matches_contiguous(causal):
+    """q, k, v, o and both scale arrays as views with a padding head between
+    rows (non-default token strides): the output equals the contiguous run
+    bit for bit and the padding head's output rows stay untouched."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    xd, bs, xf, cu = _mx_inputs(RAGGED)
+    T, H, D = xd["q"].shape
+    big = {}
+    for n in ("q", "k", "v"):
+        buf = torch.zeros((T, H + 1, D), dtype=xd[n].dtype, device="cuda")
+        buf[:, :H] = xd[n]
+        big[n] = buf[:, :H]
+    bbs = []
+    for s in bs:
+        buf = torch.full((T, H + 1, D // 32), 255, dtype=torch.uint8, device="cuda")  # padding: invalid scale
+        buf[:, :H] = s
+        bbs.append(buf[:, :H])
+    out_buf = torch.full((T, H + 1, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    for lam in (0.0, 1e-2):
+        o_ref = ssa.attn_fwd(xd["q"], xd["k"], xd["v"], cu, lam, block=RAGGED.block, causal=causal, block_scales=bs)
+        ssa.attn_fwd(big["q"], big["k"], big["v"], cu, lam, block=RAGGED.block, causal=causal,
+                     block_scales=tuple(bbs), out=out_buf[:, :H])
+        torch.cuda.synchronize()
+        assert torch.equal(out_buf[:, :H], o_ref)
+        assert torch.all(out_buf[:, H] == 7.0)
