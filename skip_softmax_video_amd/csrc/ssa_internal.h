@@ -48,6 +48,7 @@ struct LaunchParams {
   float cal_t[kMaxCalib];          // log2 thresholds of the calibration pass
   float t_bh[kMaxBHPerLaunch];     // log2 threshold per (local sequence, head)
 };
+static_assert(sizeof(LaunchParams) <= 4096, "the launch parameters travel as one kernel argument (4 KB limit)");
 
 // Kernel launchers (ssa_kernel.hip). Return a hipError_t as int.
 int launch_forward(int head_dim, int block, bool calibrate, const LaunchParams& p, void* stream);
