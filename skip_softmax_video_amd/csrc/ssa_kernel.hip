@@ -13,8 +13,8 @@
 // Work decomposition (one work-group = one Br-row Q-block of one head):
 //   * Br = Bc = BLK query rows / keys per tile; BLK/32 waves, each owning 32
 //     query rows. D = head dim. Two work-groups share a CU (<= 256 VGPRs +
-//     AGPRs per wave, 64 KB of LDS per work-group), so one work-group's
-//     softmax VALU work overlaps the other's MFMA work.
+//     AGPRs per wave, 64 KB of LDS per work-group), so each SIMD runs two
+//     waves that hide each other's LDS, barrier and memory latency.
 //   * Scores are computed transposed, S^T = K_j Q^T, with
 //     v_mfma_f32_32x32x16_bf16: lane l then holds query (l % 32) and 16 keys
 //     per 32-key block, so the per-row max and sum are in-register
