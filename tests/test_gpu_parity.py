@@ -770,3 +770,64 @@ def test_mx_strided_layout_matches_contiguous(causal):
         torch.cuda.synchronize()
         assert torch.equal(out_buf[:, :H], o_ref)
         assert torch.all(out_buf[:, H] == 7.0)
+
+
+# ---- streams and graph capture -------------------------------------------------------------------
+def test_side_stream_matches_default_stream():
+    """Forward (with counters) and calibration enqueued on a non-default
+    stream give the default-stream results bit for bit."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    x, xd, cu = _inputs(RAGGED)
+    B, H = len(cu) - 1, RAGGED.num_heads
+    o0, sk0, tot0, _ = gpu_forward(xd, cu, 1e-2, "lambda", RAGGED.block, mask=False)
+    _, c0, t0 = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, [1e-3, 1e-2], block=RAGGED.block)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sk = torch.full((B * H,), 99, dtype=torch.int64, device="cuda")
+        tot = torch.full((B * H,), 99, dtype=torch.int64, device="cuda")
+        o = ssa.attn_fwd(xd["q"], xd["k"], xd["v"], cu, 1e-2, block=RAGGED.block, skipped=sk, total=tot)
+        _, c, t = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, [1e-3, 1e-2], block=RAGGED.block)
+    side.synchronize()
+    np.testing.assert_array_equal(o.float().cpu().numpy(), o0)
+    np.testing.assert_array_equal(sk.cpu().numpy().reshape(B, H), sk0)
+    np.testing.assert_array_equal(tot.cpu().numpy().reshape(B, H), tot0)
+    assert torch.equal(c, c0) and torch.equal(t, t0)
+
+
+def test_graph_capture_replays_match_eager():
+    """The forward with counters captured in a HIP graph: every replay (with
+    eager work in between) equals the eager result, counters included, since
+    the counters are cleared by a kernel, not a memset node."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    x, xd, cu = _inputs(RAGGED)
+    B, H = len(cu) - 1, RAGGED.num_heads
+    o_e, sk_e, tot_e, _ = gpu_forward(xd, cu, 1e-2, "lambda", RAGGED.block, mask=False)
+    o = torch.empty_like(xd["q"])
+    sk = torch.zeros(B * H, dtype=torch.int64, device="cuda")
+    tot = torch.zeros(B * H, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        ssa.attn_fwd(xd["q"], xd["k"], xd["v"], cu, 1e-2, block=RAGGED.block, out=o, skipped=sk, total=tot)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ssa.attn_fwd(xd["q"], xd["k"], xd["v"], cu, 1e-2, block=RAGGED.block, out=o, skipped=sk, total=tot)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.fill_(0.0)
+        sk.fill_(12345)
+        tot.fill_(12345)
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        np.testing.assert_array_equal(o.float().cpu().numpy(), o_e)
+        np.testing.assert_array_equal(sk.cpu().numpy().reshape(B, H), sk_e)
+        np.testing.assert_array_equal(tot.cpu().numpy().reshape(B, H), tot_e)
