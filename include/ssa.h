@@ -29,6 +29,10 @@
  *    [TRITON] "Kernel backends"). Element (token t, head h, dim d) sits at
  *    t * stride_token + h * stride_head + d; D is contiguous. Base pointers
  *    must be 16-byte aligned and both strides multiples of 8 elements.
+ *    Each head's rows, up to the end of its last tile, must lie within
+ *    2^32 - 1 bytes of its first row (the kernels' buffer offsets are 32-bit:
+ *    SSA_ERR_UNSUPPORTED otherwise); with H > 1, stride_head is at most 2^47
+ *    (SSA_ERR_INVALID_ARG otherwise).
  *  - Device pointers are caller-owned device memory (e.g. torch CUDA/HIP
  *    tensors). The library allocates no device memory and keeps no state
  *    between calls; it is reentrant. GPU work is enqueued on `stream`
@@ -203,7 +207,8 @@ int ssa_calibration_sparsity(const ssa_problem* p, const int32_t* counts, const 
  * least squares of ln(scale_factor) on sparsity over the points with
  * 0 < sparsity < 1 and lambda > 0 (0 and 1 are plateaus with no slope
  * information). s_min / s_max are the smallest / largest fitted sparsity.
- * All pointers are host. Errors: SSA_ERR_INVALID_ARG, SSA_ERR_FIT_DEGENERATE. */
+ * All pointers are host. Errors: SSA_ERR_INVALID_ARG (also a NaN or infinite
+ * value in any point), SSA_ERR_FIT_DEGENERATE. */
 typedef struct ssa_calib_result {
   double a, log_a, b;  /* scale_factor = a * exp(b * s) = exp(log_a + b * s) */
   double s_min, s_max; /* observed sparsity range of the fitted points       */

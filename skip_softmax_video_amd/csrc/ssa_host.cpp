@@ -17,6 +17,8 @@ namespace {
 
 constexpr int kMaxHeads = ssa::kMaxBHPerLaunch;  // one sequence's heads must fit one launch
 
+constexpr int64_t kMaxHeadStride = (int64_t)1 << 47;
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 inline bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
@@ -28,6 +30,11 @@ int validate_problem(const ssa_problem* p) {
   if (p->num_heads > kMaxHeads) return SSA_ERR_UNSUPPORTED;
   if (!ssa::supported(p->head_dim, p->block)) return SSA_ERR_UNSUPPORTED;
   if (p->cu_seqlens[0] != 0) return SSA_ERR_INVALID_ARG;
+  // A token step beyond 32 bits cannot be addressed by the kernels' buffer
+  // offsets; a head step beyond 2^47 elements spans more than any device
+  // address range. Bounding both first keeps the products below in range.
+  if (p->stride_token > (int64_t)UINT32_MAX) return SSA_ERR_UNSUPPORTED;
+  if (p->num_heads > 1 && (p->stride_head > kMaxHeadStride || p->stride_head < 0)) return SSA_ERR_INVALID_ARG;
   for (int b = 0; b < p->batch; ++b) {
     const int64_t s = (int64_t)p->cu_seqlens[b + 1] - p->cu_seqlens[b];
     if (s < 0) return SSA_ERR_INVALID_ARG;
@@ -69,6 +76,8 @@ int validate_block_scales(const ssa_problem* p) {
   if ((uintptr_t)p->block_scale_q % row != 0 || (uintptr_t)p->block_scale_k % row != 0) return SSA_ERR_INVALID_ARG;
   const int64_t st = p->block_scale_stride_token, sh = p->block_scale_stride_head;
   if (st < row || st % row != 0 || sh < 0 || sh % row != 0) return SSA_ERR_INVALID_ARG;
+  if (sh > kMaxHeadStride) return SSA_ERR_INVALID_ARG;
+  if (st > (int64_t)UINT32_MAX) return SSA_ERR_UNSUPPORTED;
   if (p->num_heads > 1 && sh < row) return SSA_ERR_INVALID_ARG;
   for (int b = 0; b < p->batch; ++b) {
     const int64_t s = (int64_t)p->cu_seqlens[b + 1] - p->cu_seqlens[b];
@@ -245,6 +254,10 @@ int ssa_attn_fwd(const ssa_problem* p, const void* q, const void* k, const void*
     }
   int64_t nq = 0, nk = 0;
   ssa_tile_mask_dims(p, &nq, &nk);
+  int64_t mask_bytes = 0;
+  if (tile_mask && (__builtin_mul_overflow((int64_t)B * H, nq, &mask_bytes) ||
+                    __builtin_mul_overflow(mask_bytes, nk, &mask_bytes)))
+    return SSA_ERR_UNSUPPORTED;
 
   ssa::LaunchParams tmpl = base_params(p, q, k, v, o);
   tmpl.skipped_bh = skipped_bh;
@@ -258,7 +271,7 @@ int ssa_attn_fwd(const ssa_problem* p, const void* q, const void* k, const void*
   if (skipped_bh) { st = hip_status(ssa::launch_fill_u64(skipped_bh, (int64_t)B * H, stream)); if (st) return st; }
   if (total_bh) { st = hip_status(ssa::launch_fill_u64(total_bh, (int64_t)B * H, stream)); if (st) return st; }
   if (tile_mask) {
-    st = hip_status(ssa::launch_fill_u8(tile_mask, (int64_t)B * H * nq * nk, 2, stream));
+    st = hip_status(ssa::launch_fill_u8(tile_mask, mask_bytes, 2, stream));
     if (st) return st;
   }
   for (const auto& lp : plan.launches) {
@@ -325,7 +338,7 @@ int ssa_calibration_fit(const double* lambda, const double* sparsity, const doub
   std::vector<double> xs, ys;
   for (int i = 0; i < n; ++i) {
     const double s = sparsity[i], lam = lambda[i], sk = seq_k[i];
-    if (isnan(s) || isnan(lam) || isnan(sk)) return SSA_ERR_INVALID_ARG;
+    if (!isfinite(s) || !isfinite(lam) || !isfinite(sk)) return SSA_ERR_INVALID_ARG;
     if (!(s > 0.0 && s < 1.0) || !(lam > 0.0) || !(sk > 0.0)) continue;
     xs.push_back(s);
     ys.push_back(log(lam * sk));  // ln(scale_factor)

@@ -88,6 +88,12 @@ def test_fit_matches_oracle_and_degenerate():
     with pytest.raises(ssa.SSAError) as e:
         ssa.calibration_fit([1e-3, 1e-2], [0.5, 0.5], 100.0)
     assert e.value.status == ssa.SSA_ERR_FIT_DEGENERATE
+    # non-finite points are rejected, not fitted
+    for lam, s, sk in (([1e-3, np.inf], [0.3, 0.6], 100.0), ([1e-3, 1e-2], [0.3, 0.6], np.inf),
+                       ([1e-3, 1e-2], [0.3, np.nan], 100.0)):
+        with pytest.raises(ssa.SSAError) as e:
+            ssa.calibration_fit(lam, s, sk)
+        assert e.value.status == ssa.SSA_ERR_INVALID_ARG
 
 
 def test_calibration_sparsity_reduction():
@@ -148,6 +154,15 @@ FAKE = 1 << 20  # aligned, never dereferenced: validation fails first
     (dict(dtype=1, scale_q=1.0, scale_k=1.0, scale_v=1.0, stride_token=264, stride_head=136),
      (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),                          # e4m3 rows must be 16-byte aligned
     (dict(causal=-1), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    # a token step past 32-bit buffer offsets; a head step past any device range
+    (dict(stride_token=1 << 33), (0, [0.1]), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(stride_token=(1 << 62) + 128), (0, [0.1]), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(stride_head=1 << 48), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(stride_head=-128), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
+    (dict(dtype=2, block_scale_q=FAKE, block_scale_k=FAKE, block_scale_stride_token=1 << 60,
+          block_scale_stride_head=4), (0, [0.1]), ssa.SSA_ERR_UNSUPPORTED),
+    (dict(dtype=2, block_scale_q=FAKE, block_scale_k=FAKE, block_scale_stride_token=8,
+          block_scale_stride_head=1 << 60), (0, [0.1]), ssa.SSA_ERR_INVALID_ARG),
     (dict(), (0, [1.5]), ssa.SSA_ERR_THRESHOLD_RANGE),
     (dict(), (0, [float("nan")]), ssa.SSA_ERR_THRESHOLD_RANGE),
     (dict(), (1, [0.25]), ssa.SSA_ERR_THRESHOLD_RANGE),            # raw log2 > 0
