@@ -197,6 +197,21 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _check_out(t, name: str, dtypes, numel: int, device) -> None:
+    """A caller-supplied output buffer must be exactly what the kernels write:
+    the library sees only its pointer, so a short buffer would be overrun."""
+    if t is None:
+        return
+    if t.dtype not in dtypes or t.device != device or not t.is_contiguous() or t.numel() != numel:
+        kinds = "/".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name} must be a contiguous {kinds} tensor of {numel} elements on {device}")
+
+
+def _counter_dtypes():
+    import torch
+    return tuple(d for d in (torch.int64, getattr(torch, "uint64", None)) if d is not None)
+
+
 def _check_qkv(q, k, v, o, block_scales=None):
     import torch
     fp8 = _is_fp8(q)
@@ -206,15 +221,16 @@ def _check_qkv(q, k, v, o, block_scales=None):
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
         byte_typed = fp8 and (name in ("q", "k") or not mx) and name != "o"
         want = q.dtype if byte_typed else torch.bfloat16
-        if t.dtype != want or not t.is_cuda or t.dim() != 3:
-            raise ValueError(f"{name} must be a 3-D {want} device tensor [T, H, D]")
+        if t.dtype != want or not t.is_cuda or t.dim() != 3 or t.device != q.device:
+            raise ValueError(f"{name} must be a 3-D {want} device tensor [T, H, D] on q's device")
         if t.shape != q.shape or t.stride() != q.stride():
             raise ValueError(f"{name} must match q's shape and strides")
     if mx:
         T, H, D = q.shape
         qs, ks = block_scales
         for name, t in (("q scales", qs), ("k scales", ks)):
-            if t.dtype != torch.uint8 or not t.is_cuda or tuple(t.shape) != (T, H, D // 32) or t.stride(2) != 1:
+            if (t.dtype != torch.uint8 or t.device != q.device or tuple(t.shape) != (T, H, D // 32)
+                    or t.stride(2) != 1):
                 raise ValueError(f"{name} must be a uint8 device tensor [T, H, D / 32] with contiguous last dim")
         if qs.stride() != ks.stride():
             raise ValueError("q and k block scales must share strides")
@@ -254,6 +270,12 @@ def attn_fwd(q, k, v, cu_seqlens, threshold: Union[float, Sequence[float]], kind
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     _check_qkv(q, k, v, out, block_scales)
     prob, cu = make_problem(q, cu_seqlens, block, sm_scale, causal, scales, block_scales)
+    bh = (len(cu) - 1) * q.shape[1]
+    _check_out(skipped, "skipped", _counter_dtypes(), bh, q.device)
+    _check_out(total, "total", _counter_dtypes(), bh, q.device)
+    if tile_mask is not None:
+        nq, nk = tile_mask_dims(prob)
+        _check_out(tile_mask, "tile_mask", (torch.uint8,), bh * nq * nk, q.device)
     vals = np.ascontiguousarray(np.atleast_1d(np.asarray(threshold, dtype=np.float64)))
     th = Thresholds(kind=_KINDS[kind], count=vals.size, values=vals.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
     st = load_library().ssa_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.byref(th),
@@ -277,11 +299,21 @@ def attn_calibrate(q, k, v, cu_seqlens, lambdas: Sequence[float], block: int = 1
         counts = torch.empty((nwg, lam.size), dtype=torch.int32, device=q.device)
     if tiles is None:
         tiles = torch.empty((nwg,), dtype=torch.int32, device=q.device)
+    _check_out(counts, "counts", (torch.int32,), nwg * lam.size, q.device)
+    _check_out(tiles, "tiles", (torch.int32,), nwg, q.device)
     st = load_library().ssa_attn_calibrate(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                            lam.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), lam.size,
                                            _ptr(counts), _ptr(tiles), _stream(stream))
     _check(st, "ssa_attn_calibrate")
     return out, counts, tiles
+
+
+def _check_host_counts(prob: Problem, c: np.ndarray, t: np.ndarray) -> None:
+    """Host copies of a calibration pass must hold one row per work-group."""
+    nwg = calib_num_workgroups(prob)
+    if c.ndim != 2 or c.shape[0] != nwg or c.shape[1] < 1 or t.shape != (nwg,):
+        raise ValueError(f"counts must be [{nwg}, n] and tiles [{nwg}] for this problem "
+                         f"(got {c.shape} and {t.shape})")
 
 
 def calibration_sparsity(cu_seqlens, num_heads: int, head_dim: int, block: int, counts: np.ndarray,
@@ -290,10 +322,11 @@ def calibration_sparsity(cu_seqlens, num_heads: int, head_dim: int, block: int, 
     cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
     c = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
     t = np.ascontiguousarray(np.asarray(tiles, dtype=np.int32))
-    n = c.shape[1]
     prob = Problem(batch=len(cu) - 1, num_heads=num_heads, head_dim=head_dim, block=block,
                    cu_seqlens=cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                    stride_token=num_heads * head_dim, stride_head=head_dim, sm_scale=0.0)
+    _check_host_counts(prob, c, t)
+    n = c.shape[1]
     out = np.empty((len(cu) - 1, n), dtype=np.float64)
     P = ctypes.POINTER
     _check(load_library().ssa_calibration_sparsity(
@@ -307,6 +340,8 @@ def calibration_fit(lambdas, sparsity, seq_k, space: str = "log") -> CalibResult
     fit of scale_factor = a * exp(b * s)."""
     lam = np.ascontiguousarray(np.asarray(lambdas, dtype=np.float64))
     sp = np.ascontiguousarray(np.asarray(sparsity, dtype=np.float64))
+    if lam.ndim != 1 or sp.shape != lam.shape:
+        raise ValueError("lambdas and sparsity must be 1-D arrays of the same length")
     sk = np.ascontiguousarray(np.broadcast_to(np.asarray(seq_k, dtype=np.float64), lam.shape))
     res = CalibResult()
     P = ctypes.POINTER
@@ -322,6 +357,8 @@ class CalibrationPool:
     """ssa_calib_pool owned from Python: add calibration passes, read fit points."""
 
     def __init__(self, n_lambda: int, max_groups: int = 64):
+        if n_lambda < 1 or max_groups < 0:
+            raise ValueError("a pool needs n_lambda >= 1 and max_groups >= 0")
         self._seq_k = np.zeros(max_groups, dtype=np.int64)
         self._skipped = np.zeros(max_groups * n_lambda, dtype=np.int64)
         self._visited = np.zeros(max_groups, dtype=np.int64)
@@ -343,12 +380,15 @@ class CalibrationPool:
         prob = Problem(batch=len(cu) - 1, num_heads=num_heads, head_dim=128, block=block,
                        cu_seqlens=cu.ctypes.data_as(P(ctypes.c_int32)), stride_token=num_heads * 128,
                        stride_head=128, sm_scale=0.0)
+        _check_host_counts(prob, c, t)
         _check(load_library().ssa_calibration_pool_add(ctypes.byref(prob), c.ctypes.data_as(P(ctypes.c_int32)),
                                                        t.ctypes.data_as(P(ctypes.c_int32)), c.shape[1],
                                                        ctypes.byref(self.c)), "ssa_calibration_pool_add")
 
     def points(self, lambdas) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
         lam = np.ascontiguousarray(np.asarray(lambdas, dtype=np.float64))
+        if lam.shape != (self.c.n_lambda,):
+            raise ValueError(f"lambdas must hold the pool's {self.c.n_lambda} thresholds")
         m = self.c.n_groups * self.c.n_lambda
         outs = [np.empty(m, dtype=np.float64) for _ in range(3)]
         n = ctypes.c_int32()

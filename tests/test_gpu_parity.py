@@ -831,3 +831,44 @@ def test_graph_capture_replays_match_eager():
         np.testing.assert_array_equal(o.float().cpu().numpy(), o_e)
         np.testing.assert_array_equal(sk.cpu().numpy().reshape(B, H), sk_e)
         np.testing.assert_array_equal(tot.cpu().numpy().reshape(B, H), tot_e)
+
+
+def test_binding_rejects_wrong_output_buffers():
+    """Counters, tile masks and calibration outputs of the wrong size, type or
+    layout are refused before anything is launched (the library sees only
+    their pointers)."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    x, xd, cu = _inputs(RAGGED)
+    B, H = len(cu) - 1, RAGGED.num_heads
+    q, k, v = xd["q"], xd["k"], xd["v"]
+    prob, _ = ssa.make_problem(q, cu, RAGGED.block)
+    nq, nk = ssa.tile_mask_dims(prob)
+    nwg = ssa.calib_num_workgroups(prob)
+    i64 = dict(dtype=torch.int64, device="cuda")
+    bad_fwd = [
+        dict(skipped=torch.zeros(B * H - 1, **i64)),
+        dict(total=torch.zeros(B * H, dtype=torch.int32, device="cuda")),
+        dict(skipped=torch.zeros(2 * B * H, **i64)[::2]),
+        dict(skipped=torch.zeros(B * H, dtype=torch.int64)),
+        dict(tile_mask=torch.empty((B, H, nq, nk - 1), dtype=torch.uint8, device="cuda")),
+        dict(tile_mask=torch.empty((B, H, nq, nk), dtype=torch.int32, device="cuda")),
+    ]
+    for kw in bad_fwd:
+        with pytest.raises(ValueError):
+            ssa.attn_fwd(q, k, v, cu, 1e-2, block=RAGGED.block, **kw)
+    bad_cal = [
+        dict(counts=torch.empty((nwg, 1), dtype=torch.int32, device="cuda")),
+        dict(counts=torch.empty((nwg, 2), dtype=torch.int64, device="cuda")),
+        dict(tiles=torch.empty((nwg - 1,), dtype=torch.int32, device="cuda")),
+    ]
+    for kw in bad_cal:
+        with pytest.raises(ValueError):
+            ssa.attn_calibrate(q, k, v, cu, [1e-3, 1e-2], block=RAGGED.block, **kw)
+    # exactly sized buffers, in either counter type torch offers, are accepted
+    sk = torch.zeros((B, H), **i64)
+    ssa.attn_fwd(q, k, v, cu, 1e-2, block=RAGGED.block, skipped=sk,
+                 tile_mask=torch.empty((B, H, nq, nk), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    _, sk0, _, _ = gpu_forward(xd, cu, 1e-2, "lambda", RAGGED.block, mask=False)
+    np.testing.assert_array_equal(sk.cpu().numpy(), sk0)

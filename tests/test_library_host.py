@@ -346,3 +346,26 @@ def test_pool_errors_leave_it_unchanged():
     for k in before:
         np.testing.assert_array_equal(after[k][0], before[k][0])
         assert after[k][1] == before[k][1]
+
+
+def test_host_arrays_must_match_the_problem():
+    """The C functions read counts[w * n + k] for every work-group w: the
+    binding refuses host arrays of another shape before calling them."""
+    rng = np.random.default_rng(4)
+    cu, counts, tiles = _random_pass(rng, 2, 64, 4, [100, 200])
+    with pytest.raises(ValueError):
+        ssa.calibration_sparsity(cu, 2, 128, 64, counts[:-1], tiles)
+    with pytest.raises(ValueError):
+        ssa.calibration_sparsity(cu, 2, 128, 64, counts, tiles[:-1])
+    with pytest.raises(ValueError):
+        ssa.calibration_sparsity(cu, 2, 128, 64, counts.ravel(), tiles)
+    pool = ssa.CalibrationPool(4, max_groups=2)
+    with pytest.raises(ValueError):
+        pool.add(cu, 2, 64, counts[:-1], tiles[:-1])
+    pool.add(cu, 2, 64, counts, tiles)
+    with pytest.raises(ValueError):
+        pool.points(np.geomspace(1e-4, 0.5, 3))
+    with pytest.raises(ValueError):
+        ssa.CalibrationPool(0)
+    with pytest.raises(ValueError):
+        ssa.calibration_fit([1e-3, 1e-2, 1e-1], [0.3, 0.6], 100.0)
