@@ -872,3 +872,36 @@ def test_binding_rejects_wrong_output_buffers():
     torch.cuda.synchronize()
     _, sk0, _, _ = gpu_forward(xd, cu, 1e-2, "lambda", RAGGED.block, mask=False)
     np.testing.assert_array_equal(sk.cpu().numpy(), sk0)
+
+
+def test_resolved_lambda_sparsity_lies_between_calibration_points():
+    """Calibrate, fit, resolve a target, run the forward at the resolved lambda.
+    For lambda <= 1 the running maximum does not depend on lambda, so skip sets
+    are nested and each sequence's sparsity at the resolved lambda lies between
+    its calibrated sparsities at the neighbouring grid thresholds, exactly."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    cfg = RAGGED
+    x, xd, cu = _inputs(cfg)
+    B, H = len(cu) - 1, cfg.num_heads
+    lams = np.geomspace(1e-6, 0.7, 16)
+    _, counts, tiles = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, lams, block=cfg.block)
+    torch.cuda.synchronize()
+    sp = ssa.calibration_sparsity(cu, H, cfg.head_dim, cfg.block, counts.cpu().numpy(), tiles.cpu().numpy())
+    seq_k = float(cu[1] - cu[0])
+    fit = ssa.calibration_fit(lams, sp[0], seq_k)
+    for target in (0.05, 0.2):  # inside the 3,072-token sequence's calibrated range
+        status, lam, _ = ssa.resolve_threshold(int(seq_k), target_sparsity=target, a=fit.a, b=fit.b,
+                                               s_min=fit.s_min, s_max=fit.s_max)
+        assert status == ssa.SSA_OK and lams[0] <= lam <= lams[-1]
+        k = int(np.searchsorted(lams, lam, side="right")) - 1
+        _, sk, tot, _ = gpu_forward(xd, cu, lam, "lambda", cfg.block, mask=False)
+        for b in range(B):
+            if tot[b].sum() == 0:
+                continue
+            s_b = sk[b].sum() / tot[b].sum()
+            hi = sp[b][k + 1] if k + 1 < lams.size else 1.0
+            assert sp[b][k] <= s_b <= hi, (target, b, sp[b][k], s_b, hi)
+        s0 = sk[0].sum() / tot[0].sum()
+        log(f"  target {target}: lambda {lam:.4g}, sequence 0 sparsity {s0:.4f} "
+            f"(grid {sp[0][k]:.4f} .. {sp[0][min(k + 1, lams.size - 1)]:.4f})")
