@@ -306,6 +306,7 @@ def main() -> int:
     exec_tf = exec_flops / (sparse_ms * 1e-3) / 1e12
     fp8["speedup_vs_bf16_same_lambda"] = round(sparse_ms / fp8["ms"], 3)
     block_scaled["speedup_vs_bf16_same_lambda"] = round(sparse_ms / block_scaled["ms"], 3)
+    traffic = traffic_bytes()
     result = {
         "metric": "skip-softmax attn TFLOPS (dense-equiv) + speedup vs dense @S=75,600 H=40 D=128",
         "value": round(value, 2),
@@ -338,7 +339,9 @@ def main() -> int:
                         "fit_linear": {"a": fit_lin.a, "b": fit_lin.b}},
         "roofline": {"bound": "mfma", "achieved": round(exec_tf, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(exec_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_bytes(), "traffic_unit": "HBM bytes per launch (read + write)"},
+                     "traffic": traffic, "traffic_unit": "HBM bytes per launch (read + write)",
+                     # the counted bytes per launch over this run's average launch time
+                     "traffic_gbps": None if traffic is None else round(traffic / (sparse_ms * 1e-3) / 1e9, 1)},
     }
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib << 20
