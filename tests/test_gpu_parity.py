@@ -173,18 +173,20 @@ def test_untouched_memory_outside_valid_rows(head_dim, block):
     compare_outputs(o.float().cpu().numpy(), ref["o"])
 
 
-def _sampled_parity(cfg, lams, heads, per_head, causal=False):
+def _sampled_parity(cfg, lams, heads, per_head, causal=False, kind="lambda", counts_out=None):
     """Full-size launch; outputs and skip bits checked on sampled Q-blocks
-    (first, last/partial and random ones) that the oracle computes one by one."""
+    (first, last/partial and random ones) that the oracle computes one by one.
+    Each entry of `lams` is one threshold for every head, or one per head, of `kind`.
+    `counts_out`, if given, receives each launch's skipped-tile counts [B, H]."""
     x, xd, cu = _inputs(cfg)
     H, blk = cfg.num_heads, cfg.block
     scale = osk.default_sm_scale(cfg.head_dim)
     qbs = sample_qblocks(cu, H, blk, heads, per_head, seed=cfg.seed)
     fracs = []
     for lam in lams:
-        log(f"[{cfg.name}] lambda={lam} causal={causal}: GPU forward (full launch)")
-        o, sk, tot, mask = gpu_forward(xd, cu, lam, "lambda", blk, causal=causal)
-        t = t_matrix(cu, H, lam, "lambda")
+        log(f"[{cfg.name}] {kind}={np.unique(lam)} causal={causal}: GPU forward (full launch)")
+        o, sk, tot, mask = gpu_forward(xd, cu, lam, kind, blk, causal=causal)
+        t = t_matrix(cu, H, lam, kind)
         nqs = [osk.n_tiles(int(cu[b + 1] - cu[b]), blk) for b in range(len(cu) - 1)]
         want_tot = np.array([[n * (n + 1) // 2 if causal else n * n] * H for n in nqs])
         np.testing.assert_array_equal(tot, want_tot)
@@ -222,6 +224,8 @@ def _sampled_parity(cfg, lams, heads, per_head, causal=False):
         frac = sk.sum() / tot.sum()
         log(f"  sparsity {frac:.4f} band {band} band-mismatch {mism} max-abs {worst_max:.2e} mean-abs {mean:.2e}")
         fracs.append(frac)
+        if counts_out is not None:
+            counts_out.append(sk)
     return fracs
 
 
@@ -233,6 +237,20 @@ def test_wan5b_sampled_parity():
 def test_headline_sampled_parity():
     fr = _sampled_parity(CONFIGS["headline"], [0.0, 8e-3], heads=[0, 19, 39], per_head=3)
     assert fr[0] == 0.0 and fr[1] > 0.3
+
+
+def test_varlen_full_size_per_head_scale_factor():
+    """The varlen batch at full size (75,600 / 32,760 / 8,190 tokens, H=40):
+    per-head scale factors with heads 0-1 forced dense, lambda_bh = sf_h / S_b.
+    sf = 650 puts lambda near 8.6e-3 on the longest sequence."""
+    cfg = CONFIGS["varlen"]
+    sf = np.full(cfg.num_heads, 650.0)
+    sf[:2] = 0.0
+    counts = []
+    fr = _sampled_parity(cfg, [sf], heads=[0, 1, 2, 23, 39], per_head=2, kind="scale_factor", counts_out=counts)
+    sk = counts[0]
+    assert sk[:, :2].sum() == 0 and np.all(sk[:, 2:].sum(axis=1) > 0)
+    assert fr[0] > 0.3
 
 
 def test_denoising_schedule_gating():
