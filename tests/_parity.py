@@ -37,7 +37,7 @@ def to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def gpu_forward(xd: Dict, cu, threshold, kind: str, block: int, mask: bool = True, causal: bool = False,
-                block_scales=None):
+                block_scales=None, sm_scale: float = 0.0):
     """Run ssa_attn_fwd; return (o fp32 numpy [T,H,D], skipped [B,H], total [B,H], mask or None).
     `block_scales` = (q scales, k scales) selects block-scaled e4m3 q/k."""
     import torch
@@ -51,7 +51,7 @@ def gpu_forward(xd: Dict, cu, threshold, kind: str, block: int, mask: bool = Tru
         prob, _ = ssa.make_problem(xd["q"], cu, block)
         nq, nk = ssa.tile_mask_dims(prob)
         tm = torch.empty((B, H, nq, nk), dtype=torch.uint8, device="cuda")
-    o = ssa.attn_fwd(xd["q"], xd["k"], xd["v"], cu, threshold, kind=kind, block=block,
+    o = ssa.attn_fwd(xd["q"], xd["k"], xd["v"], cu, threshold, kind=kind, block=block, sm_scale=sm_scale,
                      skipped=skipped, total=total, tile_mask=tm, causal=causal, block_scales=block_scales)
     torch.cuda.synchronize()
     return (o.float().cpu().numpy(), skipped.cpu().numpy().reshape(B, H), total.cpu().numpy().reshape(B, H),

@@ -41,18 +41,21 @@ def _f64(x):
     return {n: to_f64(x[n]) for n in ("q", "k", "v")}
 
 
-def _full_parity(cfg, threshold, kind="lambda", block=None, causal=False):
+def _full_parity(cfg, threshold, kind="lambda", block=None, causal=False, sm_scale=None):
+    """Whole batch on the GPU and in the oracle; sm_scale None = the default 1/sqrt(D)."""
     block = block or cfg.block
     x, xd, cu = _inputs(cfg)
     xf = _f64(x)
     H = cfg.num_heads
-    log(f"[{cfg.name}] D={cfg.head_dim} block={block} threshold={threshold} kind={kind} causal={causal}")
-    o, sk, tot, mask = gpu_forward(xd, cu, threshold, kind, block, causal=causal)
+    log(f"[{cfg.name}] D={cfg.head_dim} block={block} threshold={threshold} kind={kind} causal={causal} "
+        f"sm_scale={sm_scale}")
+    o, sk, tot, mask = gpu_forward(xd, cu, threshold, kind, block, causal=causal, sm_scale=sm_scale or 0.0)
     t = t_matrix(cu, H, threshold, kind)
-    ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, block, causal=causal)
+    ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, block, sm_scale=sm_scale, causal=causal)
     wgs = osk.workgroups(cu, H, block)
     band, mism = compare_masks(mask, ref, t, wgs)
-    forced = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, block, forced_mask=mask, causal=causal)
+    forced = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, block, sm_scale=sm_scale,
+                                      forced_mask=mask, causal=causal)
     mx, mean = compare_outputs(o, forced["o"])
     np.testing.assert_array_equal(sk, (mask == osk.TILE_SKIPPED).sum(axis=(2, 3)))
     np.testing.assert_array_equal(tot, ref["total"])
@@ -923,3 +926,31 @@ def test_resolved_lambda_sparsity_lies_between_calibration_points():
         s0 = sk[0].sum() / tot[0].sum()
         log(f"  target {target}: lambda {lam:.4g}, sequence 0 sparsity {s0:.4f} "
             f"(grid {sp[0][k]:.4f} .. {sp[0][min(k + 1, lams.size - 1)]:.4f})")
+
+
+@pytest.mark.parametrize("sm_scale", [0.125, 0.03])
+def test_custom_sm_scale_parity(sm_scale):
+    """A caller-given softmax scale replaces 1/sqrt(D) in the scores, the skip
+    test and the softmax alike (0.125 sharpens the rows, 0.03 flattens them)."""
+    sk, tot, _, _ = _full_parity(RAGGED, 1e-2, sm_scale=sm_scale)
+    sk0, _, _, _ = _full_parity(RAGGED, 1e-2)
+    assert sk.sum() != sk0.sum()  # the scale reaches the skip test
+    if sm_scale > 1 / math.sqrt(RAGGED.head_dim):
+        assert sk.sum() > sk0.sum()
+
+
+def test_log2_thresholds_equal_lambda_thresholds():
+    """A raw log2 threshold is the kernel's own threshold: log2(lambda) given
+    directly gives the lambda call's result bit for bit, and -inf is dense."""
+    x, xd, cu = _inputs(RAGGED)
+    lam = [1e-3, 1e-2, 0.5]
+    o_l, sk_l, tot_l, m_l = gpu_forward(xd, cu, lam, "lambda", RAGGED.block)
+    o_t, sk_t, tot_t, m_t = gpu_forward(xd, cu, list(np.log2(lam)), "log2", RAGGED.block)
+    np.testing.assert_array_equal(o_t, o_l)
+    np.testing.assert_array_equal(m_t, m_l)
+    np.testing.assert_array_equal(sk_t, sk_l)
+    assert sk_l.sum() > 0
+    o_d, sk_d, _, _ = gpu_forward(xd, cu, 0.0, "lambda", RAGGED.block)
+    o_i, sk_i, _, _ = gpu_forward(xd, cu, -math.inf, "log2", RAGGED.block)
+    np.testing.assert_array_equal(o_i, o_d)
+    assert sk_i.sum() == 0 and sk_d.sum() == 0
