@@ -793,6 +793,30 @@ def test_mx_strided_layout_matches_contiguous(causal):
         assert torch.all(out_buf[:, H] == 7.0)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_strided_layout_matches_contiguous(causal):
+    """e4m3 q, k, v and the bf16 output as views with a padding head between
+    rows: the output equals the contiguous run bit for bit and the padding
+    head's output rows stay untouched."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    xd, xf, scales, cu = _fp8_inputs(RAGGED)
+    T, H, D = xd["q"].shape
+    big = {}
+    for n in ("q", "k", "v"):
+        buf = torch.full((T, H + 1, D), 0x7E, dtype=torch.uint8, device="cuda")  # padding: e4m3 448
+        buf[:, :H] = xd[n]
+        big[n] = buf[:, :H]
+    out_buf = torch.full((T, H + 1, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    for lam in (0.0, 1e-2):
+        o_ref = ssa.attn_fwd(xd["q"], xd["k"], xd["v"], cu, lam, block=RAGGED.block, causal=causal, scales=scales)
+        ssa.attn_fwd(big["q"], big["k"], big["v"], cu, lam, block=RAGGED.block, causal=causal, scales=scales,
+                     out=out_buf[:, :H])
+        torch.cuda.synchronize()
+        assert torch.equal(out_buf[:, :H], o_ref)
+        assert torch.all(out_buf[:, H] == 7.0)
+
+
 # ---- streams and graph capture -------------------------------------------------------------------
 def test_side_stream_matches_default_stream():
     """Forward (with counters) and calibration enqueued on a non-default
