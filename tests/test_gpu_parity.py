@@ -392,6 +392,17 @@ def test_calibration_all_tile_shapes(head_dim, block, causal):
     assert counts.sum() > 0
 
 
+def test_calibration_64_thresholds():
+    """The largest threshold list (64: one per lane of a wave), including a
+    repeated value: every column matches the forward at its lambda exactly."""
+    lams = np.geomspace(1e-8, 1.0, 63)
+    lams = np.sort(np.concatenate([lams, lams[40:41]]))
+    assert lams.size == 64
+    counts = _calibration_matches_forward(_shape_cfg(128, 128), lams, causal=False)
+    np.testing.assert_array_equal(counts[:, 40], counts[:, 41])
+    assert np.all(np.diff(counts, axis=1) >= 0) and counts[:, -1].sum() > counts[:, 0].sum()
+
+
 @pytest.mark.parametrize("head_dim,block", [(64, 128), (128, 64)])
 def test_causal_other_tile_shapes(head_dim, block):
     sk, tot, _, _ = _full_parity(_shape_cfg(head_dim, block), 1.0, causal=True)
