@@ -4,15 +4,16 @@ TEST INFRASTRUCTURE ONLY (see the package header): never called by the product.
 
 Sources (web pages, cited by title and section):
 * ModelOpt diffusers sparsity README "Skip-Softmax Sparse Attention for
-  Diffusion Models", introduction: KV tiles whose attention scores are
-  negligible are skipped inside the FlashAttention loop; section "Threshold
+  Diffusion Models", introduction: the FlashAttention loop leaves out KV
+  tiles that would add almost nothing to the softmax; section "Threshold
   Modes": the kernel compares in log2 units against log2(lambda).
 * ModelOpt pull request "skip-softmax ... via dedicated Triton kernels",
-  section "Changes / Triton kernels": a tile whose maximum score lies far
-  below the running softmax maximum is skipped entirely (no V load, no
-  softmax, no accumulation); runtime sparsity is counted per tile; the
-  calibration kernel computes full attention while counting, for N
-  thresholds at once, how many tiles would be skipped.
+  section "Changes / Triton kernels": when a tile's largest score sits well
+  under the running softmax maximum, the loop moves on to the next tile
+  without fetching that tile's V, exponentiating its scores or adding to the
+  output; the skipped tiles are counted at run time; the calibration kernel
+  runs the full attention and, in the same pass, counts for N thresholds
+  how many tiles each would have left out.
 * ModelOpt pull request #1166 "Add the Skip softmax for diffusion", section
   "Usage": tiles are br x bc = 128 x 128, attention is non-causal.
 

@@ -110,11 +110,15 @@ class GateSpec(ctypes.Structure):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libssa.so (built by skip_softmax_video_amd.build). Raises if absent."""
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libssa.so (built by skip_softmax_video_amd.build). Raises if absent.
+    The environment variable SSA_LIBRARY names another build to load instead
+    (the CPU sanitizer tests use it for their host-only build)."""
     global _lib
     if _lib is not None:
         return _lib
+    if path is None:
+        path = os.environ.get("SSA_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m skip_softmax_video_amd.build`; "
                            "there is no fallback implementation")
@@ -157,6 +161,28 @@ def _check(status: int, where: str) -> int:
 
 
 # ---- problem marshalling -----------------------------------------------------
+def check_cu_seqlens(cu_seqlens, num_tokens: int) -> np.ndarray:
+    """cu_seqlens as the int32 host array the library reads, checked against
+    the token count of the [T, H, D] tensors. The library sees only pointers,
+    so a last offset past T would make the kernels read q/k/v and write o
+    beyond the tensors: refused here, before any launch."""
+    raw = np.asarray(cu_seqlens)
+    if raw.ndim != 1 or raw.size < 2:
+        raise ValueError("cu_seqlens must be a 1-D array of B + 1 >= 2 token offsets")
+    if raw.dtype.kind not in "iu":
+        raise ValueError("cu_seqlens must hold integers")
+    wide = raw.astype(np.int64)
+    if wide[0] != 0:
+        raise ValueError("cu_seqlens must start at 0")
+    if np.any(np.diff(wide) < 0):
+        raise ValueError("cu_seqlens must never decrease")
+    if wide[-1] > int(num_tokens):
+        raise ValueError(f"cu_seqlens ends at {int(wide[-1])} tokens, past the tensors' {int(num_tokens)}")
+    if wide[-1] > np.iinfo(np.int32).max:
+        raise ValueError("cu_seqlens offsets must fit int32")
+    return np.ascontiguousarray(wide.astype(np.int32))
+
+
 def _is_fp8(t) -> bool:
     import torch
     return t.dtype in (torch.float8_e4m3fn, torch.uint8)
@@ -169,7 +195,7 @@ def make_problem(q, cu_seqlens, block: int, sm_scale: float = 0.0, causal: bool 
     `scales` = (scale_q, scale_k, scale_v); or e4m3 q/k bytes with
     `block_scales` = (q scales, k scales), uint8 E8M0 device tensors
     [T, H, D / 32] (MXFP8 q/k, bf16 v). Returns (struct, cu array kept alive)."""
-    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    cu = check_cu_seqlens(cu_seqlens, q.shape[0])
     T, H, D = q.shape
     fp8 = _is_fp8(q)
     sq, sk, sv = scales if scales is not None else (1.0, 1.0, 1.0)
@@ -368,18 +394,18 @@ class CalibrationPool:
                             skipped=self._skipped.ctypes.data_as(P(ctypes.c_int64)),
                             visited=self._visited.ctypes.data_as(P(ctypes.c_int64)))
 
-    def add(self, cu_seqlens, num_heads: int, block: int, counts, tiles) -> None:
-        """Add one calibration pass (host or device counts [num_wg, n] and tiles [num_wg]).
-        Only the sequence lengths, heads and block size of the pass matter here."""
+    def add(self, cu_seqlens, num_heads: int, head_dim: int, block: int, counts, tiles) -> None:
+        """Add one calibration pass (host or device counts [num_wg, n] and tiles [num_wg])
+        of a problem with these sequence lengths, heads, head_dim and block size."""
         if hasattr(counts, "cpu"):
             counts, tiles = counts.cpu().numpy(), tiles.cpu().numpy()
         cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
         c = np.ascontiguousarray(np.asarray(counts, dtype=np.int32))
         t = np.ascontiguousarray(np.asarray(tiles, dtype=np.int32))
         P = ctypes.POINTER
-        prob = Problem(batch=len(cu) - 1, num_heads=num_heads, head_dim=128, block=block,
-                       cu_seqlens=cu.ctypes.data_as(P(ctypes.c_int32)), stride_token=num_heads * 128,
-                       stride_head=128, sm_scale=0.0)
+        prob = Problem(batch=len(cu) - 1, num_heads=num_heads, head_dim=head_dim, block=block,
+                       cu_seqlens=cu.ctypes.data_as(P(ctypes.c_int32)), stride_token=num_heads * head_dim,
+                       stride_head=head_dim, sm_scale=0.0)
         _check_host_counts(prob, c, t)
         _check(load_library().ssa_calibration_pool_add(ctypes.byref(prob), c.ctypes.data_as(P(ctypes.c_int32)),
                                                        t.ctypes.data_as(P(ctypes.c_int32)), c.shape[1],

@@ -5,7 +5,7 @@ request "Add SkipSoftmax sparse attention support for visual generation"
 benchmarks (section "Benchmark": 720x1280, 81 frames, sequence length about
 75K). No prompts, weights or datasets are used: the inputs are synthetic with
 the same shapes and a distance-decaying logit structure, so that the
-fraction of negligible KV tiles behaves like a video model's.
+fraction of KV tiles that add almost nothing behaves like a video model's.
 
 Recipe (the pages fix none of the constants; each is a stated choice):
 
@@ -290,13 +290,16 @@ def make_inputs(cfg: VideoTokenConfig, heads: Sequence[int] | None = None) -> Di
 
 
 def make_random_inputs(seq_lens: Sequence[int], num_heads: int, head_dim: int, seed: int,
-                       scale: float = 1.0) -> Dict[str, np.ndarray]:
-    """Plain N(0, scale^2) bf16 Q/K/V for edge-case shapes (ragged lengths, empty sequences)."""
+                       scale: float = 1.0, v_scale: float = 1.0) -> Dict[str, np.ndarray]:
+    """Plain bf16 inputs for edge-case shapes (ragged lengths, empty sequences):
+    Q, K ~ N(0, scale^2), which sharpens the softmax rows as scale grows, and
+    V ~ N(0, v_scale^2), N(0, 1) as in every video configuration by default."""
     rng = np.random.default_rng(seed)
     T = int(sum(seq_lens))
     out = {}
     for name in ("q", "k", "v"):
-        x = (scale * rng.standard_normal((T, num_heads, head_dim))).astype(np.float32)
+        sd = v_scale if name == "v" else scale
+        x = (sd * rng.standard_normal((T, num_heads, head_dim))).astype(np.float32)
         out[name] = f32_to_bf16_bits(x)
     out["cu_seqlens"] = np.concatenate([[0], np.cumsum(seq_lens)]).astype(np.int32)
     return out

@@ -316,7 +316,7 @@ def test_pool_matches_oracle():
     pool, ref = ssa.CalibrationPool(n, max_groups=8), oc.CalibPool(n)
     for lengths in ([300, 1000, 0, 300], [1000], [77, 300, 129]):
         cu, counts, tiles = _random_pass(rng, H, block, n, lengths)
-        pool.add(cu, H, block, counts, tiles)
+        pool.add(cu, H, 128, block, counts, tiles)
         ref.add(counts, tiles, cu, H, block)
     got, exp = pool.groups, ref.groups
     assert list(got) == list(exp) == [300, 1000, 77, 129]
@@ -331,16 +331,16 @@ def test_pool_errors_leave_it_unchanged():
     rng = np.random.default_rng(3)
     pool = ssa.CalibrationPool(4, max_groups=2)
     cu, counts, tiles = _random_pass(rng, 2, 64, 4, [100, 200])
-    pool.add(cu, 2, 64, counts, tiles)
+    pool.add(cu, 2, 128, 64, counts, tiles)
     before = {k: (v[0].copy(), v[1]) for k, v in pool.groups.items()}
     cu2, counts2, tiles2 = _random_pass(rng, 2, 64, 4, [100, 300])  # a third key length: pool full
     with pytest.raises(ssa.SSAError):
-        pool.add(cu2, 2, 64, counts2, tiles2)
+        pool.add(cu2, 2, 128, 64, counts2, tiles2)
     cu3, counts3, tiles3 = _random_pass(rng, 2, 64, 3, [100])  # wrong threshold count
     with pytest.raises(ssa.SSAError):
-        pool.add(cu3, 2, 64, counts3, tiles3)
+        pool.add(cu3, 2, 128, 64, counts3, tiles3)
     with pytest.raises(ssa.SSAError):  # cu_seqlens must start at 0
-        pool.add(np.asarray(cu) + 5, 2, 64, counts, tiles)
+        pool.add(np.asarray(cu) + 5, 2, 128, 64, counts, tiles)
     after = pool.groups
     assert list(after) == list(before)
     for k in before:
@@ -361,11 +361,39 @@ def test_host_arrays_must_match_the_problem():
         ssa.calibration_sparsity(cu, 2, 128, 64, counts.ravel(), tiles)
     pool = ssa.CalibrationPool(4, max_groups=2)
     with pytest.raises(ValueError):
-        pool.add(cu, 2, 64, counts[:-1], tiles[:-1])
-    pool.add(cu, 2, 64, counts, tiles)
+        pool.add(cu, 2, 128, 64, counts[:-1], tiles[:-1])
+    pool.add(cu, 2, 128, 64, counts, tiles)
     with pytest.raises(ValueError):
         pool.points(np.geomspace(1e-4, 0.5, 3))
     with pytest.raises(ValueError):
         ssa.CalibrationPool(0)
     with pytest.raises(ValueError):
         ssa.calibration_fit([1e-3, 1e-2, 1e-1], [0.3, 0.6], 100.0)
+
+
+@pytest.mark.parametrize("cu, msg", [
+    ([0, 64, 129], "past the tensors"),      # last offset beyond T = 128
+    ([0, 96, 64], "never decrease"),
+    ([5, 64, 128], "start at 0"),
+    ([[0, 128]], "1-D"),
+    ([0], "1-D"),
+    ([0.0, 128.0], "integers"),
+])
+def test_cu_seqlens_refused_before_any_launch(cu, msg):
+    """The library sees only pointers, so the binding checks cu_seqlens against
+    the tensors' token count; a bad array raises before anything is launched
+    (these tensors live on the CPU, so a launch could not even be attempted)."""
+    import torch
+    q = torch.zeros((128, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=msg):
+        bnd.make_problem(q, cu, 128)
+    with pytest.raises(ValueError, match=msg):
+        bnd.check_cu_seqlens(cu, q.shape[0])
+
+
+def test_cu_seqlens_accepts_shorter_batches_and_empty_sequences():
+    import torch
+    q = torch.zeros((128, 2, 128), dtype=torch.bfloat16)
+    for cu in ([0, 128], [0, 0, 100], np.array([0, 64, 64, 120], dtype=np.int64), torch.tensor([0, 128])):
+        prob, arr = bnd.make_problem(q, cu, 128)
+        assert arr.dtype == np.int32 and prob.batch == len(arr) - 1

@@ -137,3 +137,36 @@ def test_forced_mask_reproduces_decisions(tiny):
     f = osk.skip_softmax_forward(x["q"], x["k"], x["v"], cu, t, cfg.block, forced_mask=r["mask"])
     np.testing.assert_array_equal(r["mask"], f["mask"])
     np.testing.assert_array_equal(r["o"], f["o"])
+
+
+def test_fast_form_equals_sequential_under_forced_masks(tiny):
+    """Under any forced decisions (first tile kept) both forms compute the
+    softmax restricted to the kept tiles' keys: the sequential loop through
+    its rescaled running sums, the fast form directly. Random masks include
+    decisions the threshold would never take (a row's maximum tile skipped),
+    so the equality does not lean on the lambda <= 1 lemma."""
+    cfg, x, cu = tiny
+    rng = np.random.default_rng(5)
+    full = osk.skip_softmax_forward(x["q"], x["k"], x["v"], cu, -INF, cfg.block)
+    for _ in range(3):
+        forced = full["mask"].copy()
+        real = forced != osk.TILE_NONE
+        draw = rng.random(forced.shape) < 0.5
+        forced[real & draw] = osk.TILE_SKIPPED
+        forced[..., 0] = np.where(forced[..., 0] == osk.TILE_NONE, osk.TILE_NONE, osk.TILE_KEPT)
+        seq = osk.skip_softmax_forward(x["q"], x["k"], x["v"], cu, -INF, cfg.block, forced_mask=forced)
+        fast = osk.skip_softmax_forward(x["q"], x["k"], x["v"], cu, -INF, cfg.block, forced_mask=forced,
+                                        fast=True)
+        np.testing.assert_array_equal(seq["mask"], forced)
+        np.testing.assert_allclose(seq["o"], fast["o"], atol=1e-12, rtol=0)
+        # and both equal the textbook softmax over the kept keys, written out directly
+        scale = osk.default_sm_scale(x["q"].shape[2])
+        for h in range(x["q"].shape[1]):
+            for i in range(forced.shape[2]):
+                keep = np.repeat(forced[0, h, i] == osk.TILE_KEPT, cfg.block)
+                rows = slice(i * cfg.block, (i + 1) * cfg.block)
+                z = x["q"][rows, h] @ x["k"][:, h].T * scale
+                z = np.where(keep[None, :], z, -np.inf)
+                p = np.exp(z - z.max(1, keepdims=True))
+                want = (p @ x["v"][:, h]) / p.sum(1, keepdims=True)
+                np.testing.assert_allclose(seq["o"][rows, h], want, atol=1e-12, rtol=0)
