@@ -51,5 +51,27 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+HOST_SOURCES = ["ssa_host.cpp", "ssa_gate.cpp", "ssa_calib.cpp"]
+
+
+def build_host_check(out_path: str, verbose: bool = False) -> str:
+    """CPU-only build of the host library for the sanitizer tests: the host
+    sources under AddressSanitizer and UndefinedBehaviorSanitizer (g++), with
+    the kernel launchers replaced by ssa_launch_check.cpp, which checks the
+    planned launches against the caller's buffer extents instead of launching.
+    Load it into a process started with the ASan runtime preloaded."""
+    cxx = shutil.which("g++") or "/usr/bin/g++"
+    cmd = [cxx, "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-Wall",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           *[os.path.join(CSRC, s) for s in HOST_SOURCES + ["ssa_launch_check.cpp"]], "-o", out_path]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"g++ failed ({res.returncode}):\n{res.stdout}{res.stderr}")
+    return out_path
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -2,8 +2,6 @@
 // threshold conversion, launch planning, calibration reduction, the
 // log-space exponential fit and threshold resolution. All entry points are
 // the C ABI declared in include/ssa.h.
-#include <hip/hip_runtime.h>
-
 #include <math.h>
 #include <stdint.h>
 #include <string.h>

@@ -50,10 +50,51 @@ struct LaunchParams {
 };
 static_assert(sizeof(LaunchParams) <= 4096, "the launch parameters travel as one kernel argument (4 KB limit)");
 
+#ifdef __HIPCC__
+#define SSA_HOST_DEVICE __host__ __device__
+#else
+#define SSA_HOST_DEVICE
+#endif
+
+// What one work-group computes: Q-block `qb` of head `h` of local sequence
+// `b`, whose S tokens start at token `tok0`, visiting `nk` KV tiles; `row`
+// is its row in the per-launch work-group numbering of the count tables.
+struct WorkItem {
+  int b, h, qb, nk, tok0, S, row;
+};
+
+// Work-group `bid` of a launch -> its work item. The hardware deals
+// work-group i to XCD i % 8; XCD x takes the logical ids
+// [x * (G / 8) + min(x, G % 8), ...), so each XCD walks consecutive Q-blocks
+// of one head and the K/V tiles they stream share that XCD's L2. Logical ids
+// run sequence-major, then head, then Q-block; in the causal form the
+// longest Q-blocks (most KV tiles) of each head come first.
+SSA_HOST_DEVICE inline WorkItem map_workgroup(const LaunchParams& p, int bid, int block) {
+  const int G = p.total_wg;
+  const int xcd = bid & 7;
+  const int L = xcd * (G >> 3) + (xcd < (G & 7) ? xcd : (G & 7)) + (bid >> 3);
+  WorkItem w;
+  w.b = 0;
+  while (w.b + 1 < p.nseq && p.wg_start[w.b + 1] <= L) ++w.b;
+  w.tok0 = p.tok_start[w.b];
+  w.S = p.tok_start[w.b + 1] - w.tok0;
+  const int nQ = (w.S + block - 1) / block;
+  const int rem = L - p.wg_start[w.b];
+  w.h = rem / nQ;
+  w.qb = p.causal ? nQ - 1 - (rem - w.h * nQ) : rem - w.h * nQ;
+  w.nk = p.causal ? w.qb + 1 : nQ;
+  w.row = p.wg_start[w.b] + w.h * nQ + w.qb;
+  return w;
+}
+
 // Kernel launchers (ssa_kernel.hip). Return a hipError_t as int.
 int launch_forward(int head_dim, int block, bool calibrate, const LaunchParams& p, void* stream);
 int launch_fill_u8(uint8_t* dst, int64_t n, uint8_t value, void* stream);
 int launch_fill_u64(uint64_t* dst, int64_t n, void* stream);
-bool supported(int head_dim, int block);
+
+// The (head_dim, block) pairs the kernels are built for.
+inline bool supported(int head_dim, int block) {
+  return (head_dim == 64 || head_dim == 128) && (block == 64 || block == 128);
+}
 
 }  // namespace ssa

@@ -3,10 +3,10 @@
 //
 // Method: ModelOpt pull request "skip-softmax ... via dedicated Triton
 // kernels", section "Changes / Triton kernels" -- inside the FlashAttention
-// loop, a KV tile whose maximum score lies far below the running softmax
-// maximum is skipped (no V load, no softmax, no accumulation); a calibration
-// variant computes full attention while counting, for N thresholds at once,
-// the tiles that would be skipped. ModelOpt README "Skip-Softmax Sparse
+// loop, when a KV tile's largest score sits well under the running softmax
+// maximum the loop moves on without fetching V, exponentiating or adding to
+// the output; a calibration variant runs the full attention and counts, for
+// N thresholds in the same pass, the tiles each would have left out. ModelOpt README "Skip-Softmax Sparse
 // Attention for Diffusion Models", section "Threshold Modes": the comparison
 // is in log2 units against log2(lambda).
 //
@@ -206,233 +206,6 @@ __device__ __forceinline__ float wave_max(float x) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
-template <int D, int BLK, bool CALIB>
-__global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {  // 2*BLK = Shape::NT
-  using SH = Shape<D, BLK>;
-  __shared__ __attribute__((aligned(1024))) uint16_t k_lds[BLK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[BLK * D];
-  __shared__ uint64_t vote[SH::NW];
-  __shared__ float dvote[SH::NW];  // calibration: each wave's maximum of x
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps tile addressing scalar
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hl = lane >> 5;
-
-  // ---- XCD-aware work-group -> (sequence, head, Q-block) ------------------
-  // Hardware dispatches work-group i to XCD i % 8; XCD x takes logical ids
-  // [x*q + min(x, r), ...) so each XCD walks consecutive Q-blocks of a head.
-  const int G = p.total_wg;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int L = xcd * (G >> 3) + min(xcd, G & 7) + (bid >> 3);
-  int b = 0;
-  while (b + 1 < p.nseq && p.wg_start[b + 1] <= L) ++b;
-  const int tok0 = p.tok_start[b];
-  const int S = p.tok_start[b + 1] - tok0;
-  const int nQ = (S + BLK - 1) / BLK;
-  const int rem = L - p.wg_start[b];
-  const int h = rem / nQ;
-  // causal: the longest Q-blocks (most KV tiles) are dispatched first
-  const int qb = p.causal ? nQ - 1 - (rem - h * nQ) : rem - h * nQ;
-  const int nK = p.causal ? qb + 1 : nQ;
-  const int row = p.wg_start[b] + h * nQ + qb;  // (sequence, head, Q-block) index of count-table rows
-  const int H = p.num_heads;
-  const int64_t head_off = (int64_t)tok0 * p.stride_tok + (int64_t)h * p.stride_head;
-  const uint16_t* kbase = p.k + head_off;
-  const uint16_t* vbase = p.v + head_off;
-
-  const uint32_t head_bytes = head_extent<D>(S, p.stride_tok);
-  dma_load<D, BLK, false>(kbase, head_bytes, k_lds, 0, p.stride_tok, wave, lane);
-
-  // ---- Q fragment: B operand of S^T = K Q^T, held for the whole loop ------
-  const int qrow = qb * BLK + wave * 32 + l32;
-  const bool qvalid = qrow < S;
-  bf16x8 qf[SH::DS];
-  {
-    const uint16_t* qp = p.q + head_off + (int64_t)(qvalid ? qrow : 0) * p.stride_tok + 8 * hl;
-#pragma unroll
-    for (int s = 0; s < SH::DS; ++s) {
-      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-      if (qvalid) raw = *reinterpret_cast<const uint4*>(qp + 16 * s);
-      qf[s] = __builtin_bit_cast(bf16x8, raw);
-    }
-  }
-
-  const float c2 = p.scale_log2;
-  const float t = CALIB ? 0.0f : p.t_bh[b * H + h];
-  const int ncal = CALIB ? p.ncal : 0;
-  const float my_t = (CALIB && lane < ncal) ? p.cal_t[lane] : INFINITY;  // lane k holds threshold k
-  int ncount = 0;
-
-  float m_true = -INFINITY;  // running max of the method (log2 units), updated on kept tiles
-  float m_use = -INFINITY;   // exponent base, m_use <= m_true < m_use + slack
-  float l = 0.0f;            // partial row sum over this lane's keys
-  floatx16 acc[SH::MB];
-#pragma unroll
-  for (int mb = 0; mb < SH::MB; ++mb) acc[mb] = floatx16{};
-  int skipped = 0;
-
-  // V^T operand read positions (ds_read_b64_tr_b16): row within a 16-key
-  // step and byte offset within the row, before the swizzle.
-  const int tr_row = 4 * hl + ((lane & 15) >> 2);
-  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int tr_elem = 4 * (lane & 1);  // element offset inside the granule
-
-  wait_dma();
-  __syncthreads();
-
-  for (int j = 0; j < nK; ++j) {
-    const int nvalid = min(BLK, S - j * BLK);
-
-    // ---- S^T = K_j Q^T (always paid) -------------------------------------
-    // operands of step s + 1 are read from LDS while step s multiplies
-    floatx16 sc[SH::KB];
-#pragma unroll
-    for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
-    bf16x8 ka[2][SH::KB];
-#pragma unroll
-    for (int kb = 0; kb < SH::KB; ++kb) ka[0][kb] = read_k<SH>(k_lds, kb, 0, l32, hl);
-#pragma unroll
-    for (int s = 0; s < SH::DS; ++s) {
-      if (s + 1 < SH::DS) {
-#pragma unroll
-        for (int kb = 0; kb < SH::KB; ++kb) ka[(s + 1) & 1][kb] = read_k<SH>(k_lds, kb, s + 1, l32, hl);
-      }
-#pragma unroll
-      for (int kb = 0; kb < SH::KB; ++kb)
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s & 1][kb], qf[s], sc[kb], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // keys past the sequence end; causal: keys after this lane's query (diagonal tile)
-    const int kmax = (p.causal && j == qb) ? min(nvalid, wave * 32 + l32 + 1) : nvalid;
-    if (p.causal ? j == qb : nvalid < BLK) {
-#pragma unroll
-      for (int kb = 0; kb < SH::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key >= kmax) sc[kb][r] = -INFINITY;
-        }
-    }
-
-    // ---- tile row max and the skip vote ----------------------------------
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < SH::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    float rowmax, x;
-    tile_margin(xhalf_max(mx), c2, m_true, rowmax, x);  // m_true = -inf gives x = +inf
-    if (!qvalid) x = -INFINITY;
-    if constexpr (CALIB) {
-      // d = max over valid rows; "some row has x >= t_k" is exactly d >= t_k
-      const float dw = wave_max(x);
-      if (lane == 0) dvote[wave] = dw;
-    } else {
-      const bool kw = wave_any(x >= t);
-      if (lane == 0) vote[wave] = kw ? 1ull : 0ull;
-    }
-    __syncthreads();  // votes visible; every wave is done reading K_j and V_{j-1}
-
-    bool keep;
-    if constexpr (CALIB) {
-      float d = dvote[0];
-#pragma unroll
-      for (int w = 1; w < SH::NW; ++w) d = fmaxf(d, dvote[w]);
-      ncount += d < my_t ? 1 : 0;  // lanes >= ncal hold +inf and are never written out
-      keep = true;
-    } else {
-      uint64_t all = vote[0];
-#pragma unroll
-      for (int w = 1; w < SH::NW; ++w) all |= vote[w];
-      keep = __builtin_amdgcn_readfirstlane(all != 0 ? 1 : 0) != 0;  // work-group uniform
-      skipped += keep ? 0 : 1;
-      if (p.tile_mask != nullptr && tid == 0)
-        p.tile_mask[((int64_t)((p.seq_abs0 + b) * H + h) * p.mask_nq + qb) * p.mask_nk + j] = keep ? 0 : 1;
-    }
-
-    if (j + 1 < nK) dma_load<D, BLK, false>(kbase, head_bytes, k_lds, (j + 1) * BLK, p.stride_tok, wave, lane);
-    bf16x8 pb[SH::KS];
-    if (keep) {
-      dma_load<D, BLK, true>(vbase, head_bytes, v_lds, j * BLK, p.stride_tok, wave, lane);
-
-      // ---- online softmax (log2 domain), overlapping the V fetch ---------
-      m_true = fmaxf(m_true, rowmax);
-      if (wave_any(rowmax > m_use + kRescaleSlack)) {
-        const float m_new = fmaxf(m_use, rowmax);
-        const float alpha = fast_exp2(m_use - m_new);  // 0 when m_use was -inf
-        l *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < SH::MB; ++mb) acc[mb] *= alpha;
-        m_use = m_new;
-      }
-      const float nm = -m_use;
-#pragma unroll
-      for (int s = 0; s < SH::KS; ++s) {
-        floatx8 e;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          e[r] = fast_exp2(fmaf(sc[s >> 1][8 * (s & 1) + r], c2, nm));
-          l += e[r];
-        }
-        pb[s] = __builtin_convertvector(e, bf16x8);
-      }
-    }
-    wait_dma();
-    __syncthreads();  // K_{j+1} and V_j visible
-
-    if (keep) {
-      // ---- O^T += V_j^T P^T ----------------------------------------------
-      // V^T operands are read two 16-key steps ahead of their MFMAs (3-deep
-      // register ring, fully unrolled); sched_barrier keeps the schedule.
-      bf16x8 va[3][SH::MB];
-#pragma unroll
-      for (int s = 0; s < 2 && s < SH::KS; ++s)
-#pragma unroll
-        for (int mb = 0; mb < SH::MB; ++mb) va[s][mb] = read_vt<SH>(v_lds, s, mb, tr_row, tr_chunk, tr_elem);
-#pragma unroll
-      for (int s = 0; s < SH::KS; ++s) {
-        if (s + 2 < SH::KS) {
-#pragma unroll
-          for (int mb = 0; mb < SH::MB; ++mb)
-            va[(s + 2) % 3][mb] = read_vt<SH>(v_lds, s + 2, mb, tr_row, tr_chunk, tr_elem);
-        }
-#pragma unroll
-        for (int mb = 0; mb < SH::MB; ++mb)
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s % 3][mb], pb[s], acc[mb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-
-  // ---- epilogue ---------------------------------------------------------
-  const float inv = 1.0f / xhalf_sum(l);
-  if (qvalid) {
-    uint16_t* op = p.o + head_off + (int64_t)qrow * p.stride_tok;
-#pragma unroll
-    for (int mb = 0; mb < SH::MB; ++mb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const floatx4 f = {acc[mb][4 * g] * inv, acc[mb][4 * g + 1] * inv, acc[mb][4 * g + 2] * inv,
-                           acc[mb][4 * g + 3] * inv};
-        const bf16x4 o4 = __builtin_convertvector(f, bf16x4);
-        *reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * g + 4 * hl) = o4;
-      }
-  }
-  if constexpr (CALIB) {
-    if (wave == 0 && lane < ncal) p.counts[(p.wg_abs0 + row) * ncal + lane] = ncount;
-    if (tid == 0) p.tiles[p.wg_abs0 + row] = nK;
-  } else {
-    if (tid == 0) {
-      const int64_t bh = (int64_t)(p.seq_abs0 + b) * H + h;
-      if (p.skipped_bh != nullptr) atomicAdd((unsigned long long*)&p.skipped_bh[bh], (unsigned long long)skipped);
-      if (p.total_bh != nullptr) atomicAdd((unsigned long long*)&p.total_bh[bh], (unsigned long long)nK);
-    }
-  }
-}
-
 // ===========================================================================
 // FP8 (OCP e4m3) variant: the same tile loop with Q K^T and P V on the
 // fp8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4, unit block scales).
@@ -536,220 +309,6 @@ __device__ __forceinline__ intx8 read_vt8(const uint8_t* v_lds, int s, int mb, c
   return r;
 }
 
-template <int D, int BLK, bool CALIB>
-__global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_fp8(const LaunchParams p) {
-  using SH = Shape8<D, BLK>;
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[BLK * D];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[BLK * D];
-  __shared__ uint64_t vote[SH::NW];
-  __shared__ float dvote[SH::NW];  // calibration: each wave's maximum of x
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hl = lane >> 5;
-
-  const int G = p.total_wg;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int L = xcd * (G >> 3) + min(xcd, G & 7) + (bid >> 3);
-  int b = 0;
-  while (b + 1 < p.nseq && p.wg_start[b + 1] <= L) ++b;
-  const int tok0 = p.tok_start[b];
-  const int S = p.tok_start[b + 1] - tok0;
-  const int nQ = (S + BLK - 1) / BLK;
-  const int rem = L - p.wg_start[b];
-  const int h = rem / nQ;
-  const int qb = p.causal ? nQ - 1 - (rem - h * nQ) : rem - h * nQ;
-  const int nK = p.causal ? qb + 1 : nQ;
-  const int row = p.wg_start[b] + h * nQ + qb;
-  const int H = p.num_heads;
-  const int64_t head_off = (int64_t)tok0 * p.stride_tok + (int64_t)h * p.stride_head;  // elements = bytes
-  const uint8_t* q8 = reinterpret_cast<const uint8_t*>(p.q);
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) + head_off;
-  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) + head_off;
-  const uint32_t head_bytes = head_extent8<D>(S, p.stride_tok);
-
-  dma_load8<D, BLK, false>(kbase, head_bytes, k_lds, 0, p.stride_tok, wave, lane);
-
-  // Q fragment: B operand of S^T = K Q^T: query qrow, d bytes [64 s + 32 hl, +32)
-  const int qrow = qb * BLK + wave * 32 + l32;
-  const bool qvalid = qrow < S;
-  intx8 qf[SH::DS];
-  {
-    const uint8_t* qp = q8 + head_off + (int64_t)(qvalid ? qrow : 0) * p.stride_tok + 32 * hl;
-#pragma unroll
-    for (int s = 0; s < SH::DS; ++s) {
-      uint4 a = make_uint4(0u, 0u, 0u, 0u), c = make_uint4(0u, 0u, 0u, 0u);
-      if (qvalid) {
-        a = *reinterpret_cast<const uint4*>(qp + 64 * s);
-        c = *reinterpret_cast<const uint4*>(qp + 64 * s + 16);
-      }
-      qf[s] = intx8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z, (int)c.w};
-    }
-  }
-
-  const float c2 = p.scale_log2;  // includes scale_q * scale_k
-  const float t = CALIB ? 0.0f : p.t_bh[b * H + h];
-  const int ncal = CALIB ? p.ncal : 0;
-  const float my_t = (CALIB && lane < ncal) ? p.cal_t[lane] : INFINITY;  // lane k holds threshold k
-  int ncount = 0;
-  float m_true = -INFINITY, m_use = -INFINITY, l = 0.0f;
-  floatx16 acc[SH::MB];
-#pragma unroll
-  for (int mb = 0; mb < SH::MB; ++mb) acc[mb] = floatx16{};
-  int skipped = 0;
-
-  // V^T transposing-read sources: source lane (2e + c) of each 16-lane group
-  // supplies key slot e of the read, columns 16 g + 8 c of the 32-wide block.
-  int tr_off[4], tr_sw[4];
-  {
-    const int e = (lane & 15) >> 1, c = lane & 1, g = (lane & 31) >> 4;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int key = 32 * (tt >> 1) + 16 * (tt & 1) + 8 * (e >> 2) + 4 * hl + (e & 3);
-      tr_off[tt] = key * (SH::CH * 16) + g * 16 + 8 * c;
-      tr_sw[tt] = swz_v8<SH::CH>(key);
-    }
-  }
-
-  wait_dma();
-  __syncthreads();
-
-  for (int j = 0; j < nK; ++j) {
-    const int nvalid = min(BLK, S - j * BLK);
-    floatx16 sc[SH::KB];
-#pragma unroll
-    for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
-#pragma unroll
-    for (int s = 0; s < SH::DS; ++s) {
-      intx8 ka[SH::KB];
-#pragma unroll
-      for (int kb = 0; kb < SH::KB; ++kb) ka[kb] = read_k8<SH>(k_lds, kb, s, l32, hl);
-#pragma unroll
-      for (int kb = 0; kb < SH::KB; ++kb)
-        sc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[kb], qf[s], sc[kb], 0, 0, 0, kE8M0One, 0,
-                                                                 kE8M0One);
-    }
-    const int kmax = (p.causal && j == qb) ? min(nvalid, wave * 32 + l32 + 1) : nvalid;
-    if (p.causal ? j == qb : nvalid < BLK) {
-#pragma unroll
-      for (int kb = 0; kb < SH::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key >= kmax) sc[kb][r] = -INFINITY;
-        }
-    }
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < SH::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    float rowmax, x;
-    tile_margin(xhalf_max(mx), c2, m_true, rowmax, x);
-    if (!qvalid) x = -INFINITY;
-    if constexpr (CALIB) {
-      const float dw = wave_max(x);
-      if (lane == 0) dvote[wave] = dw;
-    } else {
-      const bool kw = wave_any(x >= t);
-      if (lane == 0) vote[wave] = kw ? 1ull : 0ull;
-    }
-    __syncthreads();
-
-    bool keep;
-    if constexpr (CALIB) {
-      float d = dvote[0];
-#pragma unroll
-      for (int w = 1; w < SH::NW; ++w) d = fmaxf(d, dvote[w]);
-      ncount += d < my_t ? 1 : 0;
-      keep = true;
-    } else {
-      uint64_t all = vote[0];
-#pragma unroll
-      for (int w = 1; w < SH::NW; ++w) all |= vote[w];
-      keep = __builtin_amdgcn_readfirstlane(all != 0 ? 1 : 0) != 0;
-      skipped += keep ? 0 : 1;
-      if (p.tile_mask != nullptr && tid == 0)
-        p.tile_mask[((int64_t)((p.seq_abs0 + b) * H + h) * p.mask_nq + qb) * p.mask_nk + j] = keep ? 0 : 1;
-    }
-
-    if (j + 1 < nK) dma_load8<D, BLK, false>(kbase, head_bytes, k_lds, (j + 1) * BLK, p.stride_tok, wave, lane);
-    intx8 pb[SH::KS];
-    if (keep) {
-      dma_load8<D, BLK, true>(vbase, head_bytes, v_lds, j * BLK, p.stride_tok, wave, lane);
-      m_true = fmaxf(m_true, rowmax);
-      if (wave_any(rowmax > m_use + kRescaleSlack)) {
-        const float m_new = fmaxf(m_use, rowmax);
-        const float alpha = fast_exp2(m_use - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < SH::MB; ++mb) acc[mb] *= alpha;
-        m_use = m_new;
-      }
-      const float nm = -m_use;
-      // P^T for 64-key step s: byte 16 u + r is score register r of key block 2 s + u
-#pragma unroll
-      for (int s = 0; s < SH::KS; ++s)
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int kb = 2 * s + (w >> 2);
-          const int r0 = 4 * (w & 3);
-          float e0 = fast_exp2(fmaf(sc[kb][r0], c2, nm));
-          float e1 = fast_exp2(fmaf(sc[kb][r0 + 1], c2, nm));
-          float e2 = fast_exp2(fmaf(sc[kb][r0 + 2], c2, nm));
-          float e3 = fast_exp2(fmaf(sc[kb][r0 + 3], c2, nm));
-          l += (e0 + e1) + (e2 + e3);
-          int word = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-          word = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, word, true);
-          pb[s][w] = word;
-        }
-    }
-    wait_dma();
-    __syncthreads();
-
-    if (keep) {
-#pragma unroll
-      for (int s = 0; s < SH::KS; ++s) {
-        intx8 va[SH::MB];
-#pragma unroll
-        for (int mb = 0; mb < SH::MB; ++mb) va[mb] = read_vt8<SH>(v_lds, s, mb, tr_off, tr_sw);
-#pragma unroll
-        for (int mb = 0; mb < SH::MB; ++mb)
-          acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[mb], pb[s], acc[mb], 0, 0, 0, kE8M0One, 0,
-                                                                    kE8M0One);
-      }
-    }
-  }
-
-  const float inv = p.v_scale / xhalf_sum(l);
-  if (qvalid) {
-    uint16_t* op = p.o + head_off + (int64_t)qrow * p.stride_tok;
-#pragma unroll
-    for (int mb = 0; mb < SH::MB; ++mb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const floatx4 f = {acc[mb][4 * g] * inv, acc[mb][4 * g + 1] * inv, acc[mb][4 * g + 2] * inv,
-                           acc[mb][4 * g + 3] * inv};
-        const bf16x4 o4 = __builtin_convertvector(f, bf16x4);
-        *reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * g + 4 * hl) = o4;
-      }
-  }
-  if constexpr (CALIB) {
-    if (wave == 0 && lane < ncal) p.counts[(p.wg_abs0 + row) * ncal + lane] = ncount;
-    if (tid == 0) p.tiles[p.wg_abs0 + row] = nK;
-  } else {
-    if (tid == 0) {
-      const int64_t bh = (int64_t)(p.seq_abs0 + b) * H + h;
-      if (p.skipped_bh != nullptr) atomicAdd((unsigned long long*)&p.skipped_bh[bh], (unsigned long long)skipped);
-      if (p.total_bh != nullptr) atomicAdd((unsigned long long*)&p.total_bh[bh], (unsigned long long)nK);
-    }
-  }
-}
-
 // ===========================================================================
 // Block-scaled q/k (MXFP8) variant: S^T = K Q^T on the fp8 matrix cores with
 // one E8M0 scale per 32 consecutive d of every q and k row; v is bf16, and
@@ -785,69 +344,142 @@ __device__ __forceinline__ uint32_t load_scale_row(__amdgpu_buffer_rsrc_t rsrc, 
   }
 }
 
-template <int D, int BLK, bool CALIB>
-__global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_mxqk(const LaunchParams p) {
-  using SH = Shape<D, BLK>;   // bf16 V tile, softmax, P.V
-  using S8 = Shape8<D, BLK>;  // e4m3 K tile, S^T
-  constexpr int SROW = D / 32;  // scale bytes per row
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[BLK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_lds[BLK * D];
-  __shared__ uint64_t vote[SH::NW];
-  __shared__ float dvote[SH::NW];
+// ===========================================================================
+// Operand policies. The tile loop below is written once; what differs between
+// the bf16, e4m3 and block-scaled q/k modes is how Q, K and V are held and
+// multiplied, and that lives in these classes:
+//   Qk*: the Q fragment (loaded once), the K tile fetch (with its per-lane
+//        block scales in the MX mode) and S^T = K_j Q^T into 4 accumulator
+//        blocks of 32 keys;
+//   Pv*: the V tile fetch, the softmax numerator P (exponentials, the row
+//        sum and the rounding to the P.V operand type) and O^T += V_j^T P^T.
+// ===========================================================================
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hl = lane >> 5;
+// bf16 Q and K: v_mfma_f32_32x32x16_bf16 with the K operand read one d step ahead.
+template <int D, int BLK>
+struct QkBf16 {
+  using SH = Shape<D, BLK>;
+  static constexpr int LDS_BYTES = BLK * D * 2;
+  const uint16_t* kbase;
+  uint32_t bytes;
+  int64_t stride;
+  bf16x8 qf[SH::DS];
 
-  const int G = p.total_wg;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7;
-  const int L = xcd * (G >> 3) + min(xcd, G & 7) + (bid >> 3);
-  int b = 0;
-  while (b + 1 < p.nseq && p.wg_start[b + 1] <= L) ++b;
-  const int tok0 = p.tok_start[b];
-  const int S = p.tok_start[b + 1] - tok0;
-  const int nQ = (S + BLK - 1) / BLK;
-  const int rem = L - p.wg_start[b];
-  const int h = rem / nQ;
-  const int qb = p.causal ? nQ - 1 - (rem - h * nQ) : rem - h * nQ;
-  const int nK = p.causal ? qb + 1 : nQ;
-  const int row = p.wg_start[b] + h * nQ + qb;
-  const int H = p.num_heads;
-  const int64_t head_off = (int64_t)tok0 * p.stride_tok + (int64_t)h * p.stride_head;  // elements
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) + head_off;
-  const uint16_t* vbase = p.v + head_off;
-  const uint32_t k_bytes = head_extent8<D>(S, p.stride_tok);
-  const uint32_t v_bytes = head_extent<D>(S, p.stride_tok);
-  const int64_t sc_off = (int64_t)tok0 * p.bs_tok + (int64_t)h * p.bs_head;
-  const uint32_t sc_bytes = S > 0 ? (uint32_t)((int64_t)(S - 1) * p.bs_tok + SROW) : 0u;
-  const __amdgpu_buffer_rsrc_t ks_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_bscale + sc_off), 0, sc_bytes, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t qs_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.q_bscale + sc_off), 0, sc_bytes, kBufferFlags);
-
-  // K tile 0 and the scale rows of its keys (lane: key 32 kb + l32; the
-  // host keeps (S + BLK) * bs_tok within 32 bits)
-  const uint32_t sc_lane = (uint32_t)(l32 * p.bs_tok);
-  const uint32_t sc_blk = (uint32_t)(32 * p.bs_tok);  // one 32-key block
-  dma_load8<D, BLK, false>(kbase, k_bytes, k_lds, 0, p.stride_tok, wave, lane);
-  uint32_t ks[S8::KB];
+  __device__ QkBf16(const LaunchParams& p, const WorkItem& w, int64_t head_off, int qrow, bool qvalid, int hl)
+      : kbase(p.k + head_off), bytes(head_extent<D>(w.S, p.stride_tok)), stride(p.stride_tok) {
+    const uint16_t* qp = p.q + head_off + (int64_t)(qvalid ? qrow : 0) * p.stride_tok + 8 * hl;
 #pragma unroll
-  for (int kb = 0; kb < S8::KB; ++kb) ks[kb] = load_scale_row<D>(ks_rsrc, sc_lane, kb * sc_blk);
+    for (int s = 0; s < SH::DS; ++s) {
+      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+      if (qvalid) raw = *reinterpret_cast<const uint4*>(qp + 16 * s);
+      qf[s] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+  __device__ void fetch(uint8_t* lds, int j, int wave, int lane) {
+    dma_load<D, BLK, false>(kbase, bytes, reinterpret_cast<uint16_t*>(lds), j * BLK, stride, wave, lane);
+  }
+  __device__ void scores(floatx16 (&sc)[SH::KB], const uint8_t* lds, int l32, int hl) const {
+    const uint16_t* k_lds = reinterpret_cast<const uint16_t*>(lds);
+#pragma unroll
+    for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
+    bf16x8 ka[2][SH::KB];
+#pragma unroll
+    for (int kb = 0; kb < SH::KB; ++kb) ka[0][kb] = read_k<SH>(k_lds, kb, 0, l32, hl);
+#pragma unroll
+    for (int s = 0; s < SH::DS; ++s) {
+      if (s + 1 < SH::DS) {
+#pragma unroll
+        for (int kb = 0; kb < SH::KB; ++kb) ka[(s + 1) & 1][kb] = read_k<SH>(k_lds, kb, s + 1, l32, hl);
+      }
+#pragma unroll
+      for (int kb = 0; kb < SH::KB; ++kb)
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s & 1][kb], qf[s], sc[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
 
-  // Q fragment (B operand): query qrow, d bytes [64 s + 16 hl, +16) and
-  // [64 s + 32 + 16 hl, +16), and the scale of its MX block 2 s + hl
-  const int qrow = qb * BLK + wave * 32 + l32;
-  const bool qvalid = qrow < S;
-  intx8 qf[S8::DS];
-  uint32_t qsc[S8::DS];
-  {
+// e4m3 Q and K with per-tensor scales: the scaled MFMA with unit block scales
+// (the per-tensor factors are folded into the score scale on the host).
+template <int D, int BLK>
+struct QkFp8 {
+  using SH = Shape8<D, BLK>;
+  static constexpr int LDS_BYTES = BLK * D;
+  const uint8_t* kbase;
+  uint32_t bytes;
+  int64_t stride;
+  intx8 qf[SH::DS];
+
+  __device__ QkFp8(const LaunchParams& p, const WorkItem& w, int64_t head_off, int qrow, bool qvalid, int hl)
+      : kbase(reinterpret_cast<const uint8_t*>(p.k) + head_off), bytes(head_extent8<D>(w.S, p.stride_tok)),
+        stride(p.stride_tok) {
+    // B operand: query qrow, d bytes [64 s + 32 hl, +32)
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + head_off + (int64_t)(qvalid ? qrow : 0) * p.stride_tok +
+                        32 * hl;
+#pragma unroll
+    for (int s = 0; s < SH::DS; ++s) {
+      uint4 a = make_uint4(0u, 0u, 0u, 0u), c = make_uint4(0u, 0u, 0u, 0u);
+      if (qvalid) {
+        a = *reinterpret_cast<const uint4*>(qp + 64 * s);
+        c = *reinterpret_cast<const uint4*>(qp + 64 * s + 16);
+      }
+      qf[s] = intx8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z, (int)c.w};
+    }
+  }
+  __device__ void fetch(uint8_t* lds, int j, int wave, int lane) {
+    dma_load8<D, BLK, false>(kbase, bytes, lds, j * BLK, stride, wave, lane);
+  }
+  __device__ void scores(floatx16 (&sc)[SH::KB], const uint8_t* k_lds, int l32, int hl) const {
+#pragma unroll
+    for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
+#pragma unroll
+    for (int s = 0; s < SH::DS; ++s) {
+      intx8 ka[SH::KB];
+#pragma unroll
+      for (int kb = 0; kb < SH::KB; ++kb) ka[kb] = read_k8<SH>(k_lds, kb, s, l32, hl);
+#pragma unroll
+      for (int kb = 0; kb < SH::KB; ++kb)
+        sc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[kb], qf[s], sc[kb], 0, 0, 0, kE8M0One, 0,
+                                                                 kE8M0One);
+    }
+  }
+};
+
+// Block-scaled (MX) e4m3 Q and K: the scaled MFMA with one E8M0 scale per 32
+// d of every row; each lane fetches its key rows' scales with the K tile.
+template <int D, int BLK>
+struct QkMx {
+  using SH = Shape8<D, BLK>;
+  static constexpr int LDS_BYTES = BLK * D;
+  const uint8_t* kbase;
+  uint32_t bytes;
+  int64_t stride;
+  __amdgpu_buffer_rsrc_t ks_rsrc;
+  uint32_t sc_lane, sc_blk, sc_tile;
+  intx8 qf[SH::DS];
+  uint32_t qsc[SH::DS];
+  uint32_t ks[SH::KB];  // scale rows of this lane's keys in the K tile being fetched / used
+
+  __device__ QkMx(const LaunchParams& p, const WorkItem& w, int64_t head_off, int qrow, bool qvalid, int hl)
+      : kbase(reinterpret_cast<const uint8_t*>(p.k) + head_off), bytes(head_extent8<D>(w.S, p.stride_tok)),
+        stride(p.stride_tok) {
+    constexpr int SROW = D / 32;  // scale bytes per row
+    const int64_t sc_off = (int64_t)w.tok0 * p.bs_tok + (int64_t)w.h * p.bs_head;
+    const uint32_t sc_bytes = w.S > 0 ? (uint32_t)((int64_t)(w.S - 1) * p.bs_tok + SROW) : 0u;
+    ks_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_bscale + sc_off), 0, sc_bytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t qs_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.q_bscale + sc_off), 0, sc_bytes, kBufferFlags);
+    // lane: key 32 kb + l32 (the host keeps (S + BLK) * bs_tok within 32 bits)
+    const int l32 = qrow & 31;
+    sc_lane = (uint32_t)(l32 * p.bs_tok);
+    sc_blk = (uint32_t)(32 * p.bs_tok);
+    sc_tile = (uint32_t)(BLK * p.bs_tok);
+    // Q fragment (B operand): query qrow, d bytes [64 s + 16 hl, +16) and
+    // [64 s + 32 + 16 hl, +16), and the scale of its MX block 2 s + hl
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + head_off + (int64_t)(qvalid ? qrow : 0) * p.stride_tok +
                         16 * hl;
 #pragma unroll
-    for (int s = 0; s < S8::DS; ++s) {
+    for (int s = 0; s < SH::DS; ++s) {
       uint4 a = make_uint4(0u, 0u, 0u, 0u), c = make_uint4(0u, 0u, 0u, 0u);
       if (qvalid) {
         a = *reinterpret_cast<const uint4*>(qp + 64 * s);
@@ -855,24 +487,196 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_mxqk(const LaunchParams
       }
       qf[s] = intx8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z, (int)c.w};
     }
-    const uint32_t qs = load_scale_row<D>(qs_rsrc, sc_lane, (uint32_t)((qb * BLK + wave * 32) * p.bs_tok));
+    const uint32_t qs = load_scale_row<D>(qs_rsrc, sc_lane, (uint32_t)((qrow - l32) * p.bs_tok));
 #pragma unroll
-    for (int s = 0; s < S8::DS; ++s) qsc[s] = qs >> (8 * (2 * s + hl));  // byte 0: this lane's block
+    for (int s = 0; s < SH::DS; ++s) qsc[s] = qs >> (8 * (2 * s + hl));  // byte 0: this lane's block
   }
+  __device__ void fetch(uint8_t* lds, int j, int wave, int lane) {
+    dma_load8<D, BLK, false>(kbase, bytes, lds, j * BLK, stride, wave, lane);
+#pragma unroll
+    for (int kb = 0; kb < SH::KB; ++kb) ks[kb] = load_scale_row<D>(ks_rsrc, sc_lane, j * sc_tile + kb * sc_blk);
+  }
+  __device__ void scores(floatx16 (&sc)[SH::KB], const uint8_t* k_lds, int l32, int hl) const {
+#pragma unroll
+    for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
+#pragma unroll
+    for (int s = 0; s < SH::DS; ++s) {
+      intx8 ka[SH::KB];
+#pragma unroll
+      for (int kb = 0; kb < SH::KB; ++kb) ka[kb] = read_k8_mx<SH>(k_lds, kb, s, l32, hl);
+#pragma unroll
+      for (int kb = 0; kb < SH::KB; ++kb)
+        sc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[kb], qf[s], sc[kb], 0, 0, 0,
+                                                                 (int)(ks[kb] >> (8 * (2 * s + hl))), 0, (int)qsc[s]);
+    }
+  }
+};
+
+// bf16 V and P: P rounded to bf16 feeds O^T += V^T P^T directly from the
+// score registers; V^T comes from the row-major V tile through transposing
+// LDS reads, two 16-key steps ahead of their MFMAs.
+template <int D, int BLK>
+struct PvBf16 {
+  using SH = Shape<D, BLK>;
+  static constexpr int LDS_BYTES = BLK * D * 2;
+  using PFrag = bf16x8[SH::KS];
+  const uint16_t* vbase;
+  uint32_t bytes;
+  int64_t stride;
+  int tr_row, tr_chunk, tr_elem;  // V^T read position: row in a 16-key step, granule, element
+
+  __device__ PvBf16(const LaunchParams& p, const WorkItem& w, int64_t head_off, int lane)
+      : vbase(p.v + head_off), bytes(head_extent<D>(w.S, p.stride_tok)), stride(p.stride_tok) {
+    const int hl = lane >> 5;
+    tr_row = 4 * hl + ((lane & 15) >> 2);
+    tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    tr_elem = 4 * (lane & 1);
+  }
+  __device__ static float out_scale(const LaunchParams&) { return 1.0f; }
+  __device__ void fetch(uint8_t* lds, int j, int wave, int lane) {
+    dma_load<D, BLK, true>(vbase, bytes, reinterpret_cast<uint16_t*>(lds), j * BLK, stride, wave, lane);
+  }
+  // P = 2^(s * c2 - m) in the slot order of the P.V B operand; l += row sum
+  __device__ static void make_p(const floatx16 (&sc)[BLK / 32], float c2, float nm, float& l, PFrag& pb) {
+#pragma unroll
+    for (int s = 0; s < SH::KS; ++s) {
+      floatx8 e;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        e[r] = fast_exp2(fmaf(sc[s >> 1][8 * (s & 1) + r], c2, nm));
+        l += e[r];
+      }
+      pb[s] = __builtin_convertvector(e, bf16x8);
+    }
+  }
+  __device__ void accumulate(floatx16 (&acc)[SH::MB], const uint8_t* lds, const PFrag& pb) const {
+    const uint16_t* v_lds = reinterpret_cast<const uint16_t*>(lds);
+    bf16x8 va[3][SH::MB];
+#pragma unroll
+    for (int s = 0; s < 2 && s < SH::KS; ++s)
+#pragma unroll
+      for (int mb = 0; mb < SH::MB; ++mb) va[s][mb] = read_vt<SH>(v_lds, s, mb, tr_row, tr_chunk, tr_elem);
+#pragma unroll
+    for (int s = 0; s < SH::KS; ++s) {
+      if (s + 2 < SH::KS) {
+#pragma unroll
+        for (int mb = 0; mb < SH::MB; ++mb)
+          va[(s + 2) % 3][mb] = read_vt<SH>(v_lds, s + 2, mb, tr_row, tr_chunk, tr_elem);
+      }
+#pragma unroll
+      for (int mb = 0; mb < SH::MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s % 3][mb], pb[s], acc[mb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+// e4m3 V with a per-tensor scale: P rounded to e4m3 (two values per
+// v_cvt_pk_fp8_f32), V^T gathered by transposing byte reads, P.V on the
+// scaled MFMA with unit block scales; O carries scale_v.
+template <int D, int BLK>
+struct PvFp8 {
+  using SH = Shape8<D, BLK>;
+  static constexpr int LDS_BYTES = BLK * D;
+  using PFrag = intx8[SH::KS];
+  const uint8_t* vbase;
+  uint32_t bytes;
+  int64_t stride;
+  int tr_off[4], tr_sw[4];
+
+  __device__ PvFp8(const LaunchParams& p, const WorkItem& w, int64_t head_off, int lane)
+      : vbase(reinterpret_cast<const uint8_t*>(p.v) + head_off), bytes(head_extent8<D>(w.S, p.stride_tok)),
+        stride(p.stride_tok) {
+    // source lane (2e + c) of each 16-lane group supplies key slot e of a
+    // transposing read, columns 16 g + 8 c of the 32-wide d block
+    const int hl = lane >> 5;
+    const int e = (lane & 15) >> 1, c = lane & 1, g = (lane & 31) >> 4;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const int key = 32 * (tt >> 1) + 16 * (tt & 1) + 8 * (e >> 2) + 4 * hl + (e & 3);
+      tr_off[tt] = key * (SH::CH * 16) + g * 16 + 8 * c;
+      tr_sw[tt] = swz_v8<SH::CH>(key);
+    }
+  }
+  __device__ static float out_scale(const LaunchParams& p) { return p.v_scale; }
+  __device__ void fetch(uint8_t* lds, int j, int wave, int lane) {
+    dma_load8<D, BLK, true>(vbase, bytes, lds, j * BLK, stride, wave, lane);
+  }
+  // P^T for 64-key step s: byte 16 u + r is score register r of key block 2 s + u
+  __device__ static void make_p(const floatx16 (&sc)[BLK / 32], float c2, float nm, float& l, PFrag& pb) {
+#pragma unroll
+    for (int s = 0; s < SH::KS; ++s)
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const int kb = 2 * s + (w >> 2);
+        const int r0 = 4 * (w & 3);
+        float e0 = fast_exp2(fmaf(sc[kb][r0], c2, nm));
+        float e1 = fast_exp2(fmaf(sc[kb][r0 + 1], c2, nm));
+        float e2 = fast_exp2(fmaf(sc[kb][r0 + 2], c2, nm));
+        float e3 = fast_exp2(fmaf(sc[kb][r0 + 3], c2, nm));
+        l += (e0 + e1) + (e2 + e3);
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, word, true);
+        pb[s][w] = word;
+      }
+  }
+  __device__ void accumulate(floatx16 (&acc)[SH::MB], const uint8_t* v_lds, const PFrag& pb) const {
+#pragma unroll
+    for (int s = 0; s < SH::KS; ++s) {
+      intx8 va[SH::MB];
+#pragma unroll
+      for (int mb = 0; mb < SH::MB; ++mb) va[mb] = read_vt8<SH>(v_lds, s, mb, tr_off, tr_sw);
+#pragma unroll
+      for (int mb = 0; mb < SH::MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[mb], pb[s], acc[mb], 0, 0, 0, kE8M0One, 0,
+                                                                  kE8M0One);
+    }
+  }
+};
+
+// ===========================================================================
+// The tile loop (forward and calibration), one work-group per Q-block.
+// ===========================================================================
+template <int D, int BLK, class QK, class PV, bool CALIB>
+__global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {  // 2*BLK = 64 * BLK / 32 threads
+  constexpr int NW = BLK / 32;  // waves, 32 query rows each
+  constexpr int KB = BLK / 32;  // 32-key blocks of S^T
+  constexpr int MB = D / 32;    // 32-wide d blocks of O^T
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[QK::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds[PV::LDS_BYTES];
+  __shared__ uint64_t vote[NW];
+  __shared__ float dvote[NW];  // calibration: each wave's maximum of x
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps tile addressing scalar
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  const WorkItem w = map_workgroup(p, blockIdx.x, BLK);
+  const int b = w.b, h = w.h, qb = w.qb, nK = w.nk, S = w.S;
+  const int H = p.num_heads;
+  const int64_t head_off = (int64_t)w.tok0 * p.stride_tok + (int64_t)h * p.stride_head;  // elements
+
+  const int qrow = qb * BLK + wave * 32 + l32;
+  const bool qvalid = qrow < S;
+  QK qk(p, w, head_off, qrow, qvalid, hl);
+  qk.fetch(k_lds, 0, wave, lane);
+  PV pv(p, w, head_off, lane);
 
   const float c2 = p.scale_log2;
   const float t = CALIB ? 0.0f : p.t_bh[b * H + h];
   const int ncal = CALIB ? p.ncal : 0;
-  const float my_t = (CALIB && lane < ncal) ? p.cal_t[lane] : INFINITY;
+  const float my_t = (CALIB && lane < ncal) ? p.cal_t[lane] : INFINITY;  // lane k holds threshold k
   int ncount = 0;
-  float m_true = -INFINITY, m_use = -INFINITY, l = 0.0f;
-  floatx16 acc[SH::MB];
+
+  float m_true = -INFINITY;  // running max of the method (log2 units), updated on kept tiles
+  float m_use = -INFINITY;   // exponent base, m_use <= m_true < m_use + slack
+  float l = 0.0f;            // partial row sum over this lane's keys
+  floatx16 acc[MB];
 #pragma unroll
-  for (int mb = 0; mb < SH::MB; ++mb) acc[mb] = floatx16{};
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx16{};
   int skipped = 0;
-  const int tr_row = 4 * hl + ((lane & 15) >> 2);
-  const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int tr_elem = 4 * (lane & 1);
 
   wait_dma();
   __syncthreads();
@@ -880,24 +684,14 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_mxqk(const LaunchParams
   for (int j = 0; j < nK; ++j) {
     const int nvalid = min(BLK, S - j * BLK);
 
-    // ---- S^T = K_j Q^T with the block scales (always paid) ---------------
-    floatx16 sc[SH::KB];
-#pragma unroll
-    for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
-#pragma unroll
-    for (int s = 0; s < S8::DS; ++s) {
-      intx8 ka[S8::KB];
-#pragma unroll
-      for (int kb = 0; kb < S8::KB; ++kb) ka[kb] = read_k8_mx<S8>(k_lds, kb, s, l32, hl);
-#pragma unroll
-      for (int kb = 0; kb < S8::KB; ++kb)
-        sc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[kb], qf[s], sc[kb], 0, 0, 0,
-                                                                 (int)(ks[kb] >> (8 * (2 * s + hl))), 0, (int)qsc[s]);
-    }
+    // ---- S^T = K_j Q^T (always paid) -------------------------------------
+    floatx16 sc[KB];
+    qk.scores(sc, k_lds, l32, hl);
+    // keys past the sequence end; causal: keys after this lane's query (diagonal tile)
     const int kmax = (p.causal && j == qb) ? min(nvalid, wave * 32 + l32 + 1) : nvalid;
     if (p.causal ? j == qb : nvalid < BLK) {
 #pragma unroll
-      for (int kb = 0; kb < SH::KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
@@ -908,13 +702,14 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_mxqk(const LaunchParams
     // ---- tile row max and the skip vote ----------------------------------
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < SH::KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
     float rowmax, x;
-    tile_margin(xhalf_max(mx), c2, m_true, rowmax, x);
+    tile_margin(xhalf_max(mx), c2, m_true, rowmax, x);  // m_true = -inf gives x = +inf
     if (!qvalid) x = -INFINITY;
     if constexpr (CALIB) {
+      // d = max over valid rows; "some row has x >= t_k" is exactly d >= t_k
       const float dw = wave_max(x);
       if (lane == 0) dvote[wave] = dw;
     } else {
@@ -927,78 +722,49 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_mxqk(const LaunchParams
     if constexpr (CALIB) {
       float d = dvote[0];
 #pragma unroll
-      for (int w = 1; w < SH::NW; ++w) d = fmaxf(d, dvote[w]);
-      ncount += d < my_t ? 1 : 0;
+      for (int v = 1; v < NW; ++v) d = fmaxf(d, dvote[v]);
+      ncount += d < my_t ? 1 : 0;  // lanes >= ncal hold +inf and are never written out
       keep = true;
     } else {
       uint64_t all = vote[0];
 #pragma unroll
-      for (int w = 1; w < SH::NW; ++w) all |= vote[w];
-      keep = __builtin_amdgcn_readfirstlane(all != 0 ? 1 : 0) != 0;
+      for (int v = 1; v < NW; ++v) all |= vote[v];
+      keep = __builtin_amdgcn_readfirstlane(all != 0 ? 1 : 0) != 0;  // work-group uniform
       skipped += keep ? 0 : 1;
       if (p.tile_mask != nullptr && tid == 0)
         p.tile_mask[((int64_t)((p.seq_abs0 + b) * H + h) * p.mask_nq + qb) * p.mask_nk + j] = keep ? 0 : 1;
     }
 
-    if (j + 1 < nK) {
-      dma_load8<D, BLK, false>(kbase, k_bytes, k_lds, (j + 1) * BLK, p.stride_tok, wave, lane);
-#pragma unroll
-      for (int kb = 0; kb < S8::KB; ++kb)
-        ks[kb] = load_scale_row<D>(ks_rsrc, sc_lane, (uint32_t)((j + 1) * BLK * p.bs_tok) + kb * sc_blk);
-    }
-    bf16x8 pb[SH::KS];
+    if (j + 1 < nK) qk.fetch(k_lds, j + 1, wave, lane);
+    typename PV::PFrag pb;
     if (keep) {
-      dma_load<D, BLK, true>(vbase, v_bytes, v_lds, j * BLK, p.stride_tok, wave, lane);
+      pv.fetch(v_lds, j, wave, lane);
+
+      // ---- online softmax (log2 domain), overlapping the V fetch ---------
       m_true = fmaxf(m_true, rowmax);
       if (wave_any(rowmax > m_use + kRescaleSlack)) {
         const float m_new = fmaxf(m_use, rowmax);
-        const float alpha = fast_exp2(m_use - m_new);
+        const float alpha = fast_exp2(m_use - m_new);  // 0 when m_use was -inf
         l *= alpha;
 #pragma unroll
-        for (int mb = 0; mb < SH::MB; ++mb) acc[mb] *= alpha;
+        for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
         m_use = m_new;
       }
-      const float nm = -m_use;
-#pragma unroll
-      for (int s = 0; s < SH::KS; ++s) {
-        floatx8 e;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          e[r] = fast_exp2(fmaf(sc[s >> 1][8 * (s & 1) + r], c2, nm));
-          l += e[r];
-        }
-        pb[s] = __builtin_convertvector(e, bf16x8);
-      }
+      PV::make_p(sc, c2, -m_use, l, pb);
     }
     wait_dma();
-    __syncthreads();  // K_{j+1}, its scales and V_j visible
+    __syncthreads();  // K_{j+1} (and its scales) and V_j visible
 
-    if (keep) {
-      bf16x8 va[3][SH::MB];
-#pragma unroll
-      for (int s = 0; s < 2 && s < SH::KS; ++s)
-#pragma unroll
-        for (int mb = 0; mb < SH::MB; ++mb) va[s][mb] = read_vt<SH>(v_lds, s, mb, tr_row, tr_chunk, tr_elem);
-#pragma unroll
-      for (int s = 0; s < SH::KS; ++s) {
-        if (s + 2 < SH::KS) {
-#pragma unroll
-          for (int mb = 0; mb < SH::MB; ++mb)
-            va[(s + 2) % 3][mb] = read_vt<SH>(v_lds, s + 2, mb, tr_row, tr_chunk, tr_elem);
-        }
-#pragma unroll
-        for (int mb = 0; mb < SH::MB; ++mb)
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s % 3][mb], pb[s], acc[mb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    // ---- O^T += V_j^T P^T ------------------------------------------------
+    if (keep) pv.accumulate(acc, v_lds, pb);
   }
 
-  const float inv = 1.0f / xhalf_sum(l);
+  // ---- epilogue ---------------------------------------------------------
+  const float inv = PV::out_scale(p) / xhalf_sum(l);
   if (qvalid) {
     uint16_t* op = p.o + head_off + (int64_t)qrow * p.stride_tok;
 #pragma unroll
-    for (int mb = 0; mb < SH::MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const floatx4 f = {acc[mb][4 * g] * inv, acc[mb][4 * g + 1] * inv, acc[mb][4 * g + 2] * inv,
@@ -1008,8 +774,8 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel_mxqk(const LaunchParams
       }
   }
   if constexpr (CALIB) {
-    if (wave == 0 && lane < ncal) p.counts[(p.wg_abs0 + row) * ncal + lane] = ncount;
-    if (tid == 0) p.tiles[p.wg_abs0 + row] = nK;
+    if (wave == 0 && lane < ncal) p.counts[(p.wg_abs0 + w.row) * ncal + lane] = ncount;
+    if (tid == 0) p.tiles[p.wg_abs0 + w.row] = nK;
   } else {
     if (tid == 0) {
       const int64_t bh = (int64_t)(p.seq_abs0 + b) * H + h;
@@ -1031,15 +797,13 @@ __global__ void fill_u64_kernel(uint64_t* dst, int64_t n) {
 
 template <int D, int BLK, bool CALIB>
 int launch(const LaunchParams& p, hipStream_t stream) {
+  const dim3 grid(p.total_wg), threads(2 * BLK);  // BLK / 32 waves
   if (p.fp8) {
-    using SH = Shape8<D, BLK>;
-    hipLaunchKernelGGL((fwd_kernel_fp8<D, BLK, CALIB>), dim3(p.total_wg), dim3(SH::NT), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, BLK, QkFp8<D, BLK>, PvFp8<D, BLK>, CALIB>), grid, threads, 0, stream, p);
   } else if (p.mxqk) {
-    using SH = Shape<D, BLK>;
-    hipLaunchKernelGGL((fwd_kernel_mxqk<D, BLK, CALIB>), dim3(p.total_wg), dim3(SH::NT), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, BLK, QkMx<D, BLK>, PvBf16<D, BLK>, CALIB>), grid, threads, 0, stream, p);
   } else {
-    using SH = Shape<D, BLK>;
-    hipLaunchKernelGGL((fwd_kernel<D, BLK, CALIB>), dim3(p.total_wg), dim3(SH::NT), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, BLK, QkBf16<D, BLK>, PvBf16<D, BLK>, CALIB>), grid, threads, 0, stream, p);
   }
   return (int)hipGetLastError();
 }
@@ -1050,10 +814,6 @@ int grid_for(int64_t n) {
 }
 
 }  // namespace
-
-bool supported(int head_dim, int block) {
-  return (head_dim == 64 || head_dim == 128) && (block == 64 || block == 128);
-}
 
 int launch_forward(int head_dim, int block, bool calibrate, const LaunchParams& p, void* stream) {
   hipStream_t s = (hipStream_t)stream;
