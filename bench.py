@@ -91,37 +91,79 @@ def traffic_bytes():
     return int(TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"])
 
 
-def cpu_baseline(x, cu, t_log2: float, block: int, budget_s: float):
-    """Time the fp64 oracle (as it stands) on a bounded sample of Q-blocks."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_qblocks(x, cu, h: int, qblocks, t_log2: float, block: int):
+    """Run the fp64 oracle's tile loop (as it stands) on the given Q-blocks of
+    head h of sequence 0; returns (seconds, dense-equivalent FLOP)."""
     import numpy as np
     from oracle import skip_softmax as osk
     from synth import bf16_bits_to_f32
 
-    H = x["q"].shape[1]
     D = x["q"].shape[2]
     S = int(cu[1] - cu[0])
-    nq = osk.n_tiles(S, block)
     scale = osk.default_sm_scale(D)
-    rng = np.random.default_rng(0)
-    h = int(rng.integers(H))
-    kh = bf16_bits_to_f32(x["k"][:, h]).astype(np.float64)
-    vh = bf16_bits_to_f32(x["v"][:, h]).astype(np.float64)
-    order = rng.permutation(nq)
-    flops, done = 0.0, 0
+    kh = bf16_bits_to_f32(x["k"][:S, h]).astype(np.float64)
+    vh = bf16_bits_to_f32(x["v"][:S, h]).astype(np.float64)
+    flops = 0.0
     t0 = time.perf_counter()
-    for i in order:
+    for i in qblocks:
         r0, r1 = int(i) * block, min(S, (int(i) + 1) * block)
         qh = bf16_bits_to_f32(x["q"][r0:r1, h]).astype(np.float64)
         osk.skip_softmax_qblock(qh, kh, vh, t_log2, block, scale)
         flops += 4.0 * (r1 - r0) * S * D
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
+    return time.perf_counter() - t0, flops
+
+
+def cpu_baseline(x, cu, t_log2: float, block: int, gpu_ms: float, wan5b: bool):
+    """The fp64 oracle (as it stands) on the host cores: one full head of the
+    headline call at the calibrated lambda, timed, with the x H extrapolation
+    to the whole call labelled as such; optionally the whole WAN-5B-like call
+    (lambda = 1e-3) timed end to end."""
+    from oracle import skip_softmax as osk
+
+    H = x["q"].shape[1]
+    S = int(cu[1] - cu[0])
+    nq = osk.n_tiles(S, block)
+    h = 0
+    dt, flops = _oracle_qblocks(x, cu, h, range(nq), t_log2, block)
     threads = blas_threads()
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s (dense-equiv)", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {nq} Q-blocks of head {h} (sequential fp64 tile loop at the calibrated "
-                      f"lambda), {dt:.1f} s, numpy/BLAS threads={threads}"}
+    tflops = flops / dt / 1e12
+    out = {"value": round(tflops, 4), "unit": "TFLOP/s (dense-equiv)", "cores": threads, "kind": "oracle",
+           "sample": f"all {nq} Q-blocks of head {h} of the headline call (sequential fp64 tile loop at the "
+                     f"calibrated lambda): {dt:.1f} s",
+           "host_cpu": cpu_model(), "host_logical_cpus": os.cpu_count(),
+           "host_cpus_usable": len(os.sched_getaffinity(0)), "blas_threads": threads,
+           "one_head_s": round(dt, 2),
+           "full_call_s_extrapolated": round(dt * H, 1),
+           "extrapolation": f"one head x {H} heads (every head has the same shape; not run)",
+           "gpu_ms_same_call": round(gpu_ms, 3),
+           "gpu_speedup_over_cpu_extrapolated": round(dt * H / (gpu_ms * 1e-3), 1)}
+    if wan5b:
+        from synth import CONFIGS, make_inputs
+        cfg = CONFIGS["wan5b"]
+        xw = make_inputs(cfg)
+        cw = xw["cu_seqlens"]
+        Sw = int(cw[1])
+        t0 = time.perf_counter()
+        total_fl = 0.0
+        for hh in range(cfg.num_heads):
+            _, fl = _oracle_qblocks(xw, cw, hh, range(osk.n_tiles(Sw, cfg.block)), math.log2(1e-3), cfg.block)
+            total_fl += fl
+        dtw = time.perf_counter() - t0
+        out["wan5b_full_call"] = {"seconds": round(dtw, 2), "tflops_dense_equiv": round(total_fl / dtw / 1e12, 4),
+                                  "what": f"whole WAN-5B-like call (H={cfg.num_heads}, S={Sw}, D={cfg.head_dim}) "
+                                          f"at lambda 1e-3, sequential fp64 tile loop, run"}
+    return out
 
 
 def main() -> int:
@@ -129,8 +171,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-wan5b", action="store_true", help="skip timing the whole WAN-5B-like call on the CPU")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (scale for HBM counters)")
     args = ap.parse_args()
@@ -210,16 +252,45 @@ def main() -> int:
     log("timing calibrated mode")
     sparse_ms = time_launches(fwd(lam07), args.warmup, args.steps)
 
-    # context points (not the headline): the resolved 0.5 target and lambda = 1
-    sweep = []
-    for tag, lam in (("target 0.5", resolved["0.5"]["lambda"]), ("lambda 1", 1.0)):
+    # context points (not the headline): the resolved 0.5 target, the calibrated
+    # 0.7 point, the lambda whose achieved tile sparsity is 0.70 (bisected on the
+    # GPU's own skip counts; skip sets are nested in lambda) and lambda = 1. For
+    # each: r = (skipped-tile time) / (kept-tile time) from t / t_dense = (1 - s) + s r,
+    # and the speedup two equally efficient tile kinds would give, 1 / (1 - s / 2).
+    def sparsity_at(lam):
         ssa.attn_fwd(dx["q"], dx["k"], dx["v"], cu, lam, block=blk, out=o, skipped=skipped, total=total)
         torch.cuda.synchronize()
-        sp_l = float(skipped.sum()) / float(total.sum())
-        ms_l = time_launches(fwd(lam), 1, max(2, args.steps // 2))
-        sweep.append({"point": tag, "lambda": lam, "achieved_tile_sparsity": round(sp_l, 4), "ms": round(ms_l, 3),
-                      "speedup_vs_dense": round(dense_ms / ms_l, 3)})
-        log(f"{tag}: lambda {lam:.4g} sparsity {sp_l:.4f} {ms_l:.2f} ms")
+        return float(skipped.sum()) / float(total.sum())
+
+    lo, hi = math.log(lam07), 0.0  # sparsity(lam07) < 0.70 <= sparsity(1) on this workload
+    s_lo, s_hi = s_ach, sparsity_at(1.0)
+    lam70, s70 = None, None
+    if s_lo < 0.70 <= s_hi:
+        for _ in range(24):
+            mid = 0.5 * (lo + hi)
+            s_mid = sparsity_at(math.exp(mid))
+            if s_mid < 0.70:
+                lo, s_lo = mid, s_mid
+            else:
+                hi, s_hi = mid, s_mid
+        lam70, s70 = math.exp(hi), s_hi
+    log(f"achieved-0.70 point: lambda {lam70} sparsity {s70}")
+
+    def point(tag, lam, ms_l, sp_l):
+        r = (ms_l / dense_ms - (1.0 - sp_l)) / sp_l if sp_l > 0 else None
+        return {"point": tag, "lambda": lam, "achieved_tile_sparsity": round(sp_l, 4), "ms": round(ms_l, 3),
+                "speedup_vs_dense": round(dense_ms / ms_l, 3), "r_skipped_over_kept": None if r is None else round(r, 3),
+                "speedup_if_equal_tile_efficiency": round(1.0 / (1.0 - sp_l / 2.0), 3)}
+
+    sweep = []
+    for tag, lam in (("target 0.5", resolved["0.5"]["lambda"]), ("calibrated target 0.7", lam07),
+                     ("achieved sparsity 0.70", lam70), ("lambda 1", 1.0)):
+        if lam is None:
+            continue
+        sp_l = sparsity_at(lam)
+        ms_l = sparse_ms if lam == lam07 else time_launches(fwd(lam), 1, max(2, args.steps // 2))
+        sweep.append(point(tag, lam, ms_l, sp_l))
+        log(f"{tag}: lambda {lam:.4g} sparsity {sp_l:.4f} {ms_l:.2f} ms r {sweep[-1]['r_skipped_over_kept']}")
 
     # causal (prefill) form of the same shape: dense and calibrated lambda
     causal_fwd = lambda lam: (lambda: ssa.attn_fwd(dx["q"], dx["k"], dx["v"], cu, lam, block=blk, out=o, causal=True))
@@ -354,7 +425,7 @@ def main() -> int:
         del src, dst
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(x, cu, math.log2(lam07), blk, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(x, cu, math.log2(lam07), blk, sparse_ms, not args.no_cpu_wan5b)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -6,6 +6,7 @@ through `oracle/`; both consume the same `synth` bf16 inputs.
 from __future__ import annotations
 
 import math
+import os
 import sys
 from typing import Dict, Iterable, Optional, Sequence, Tuple
 
@@ -111,20 +112,113 @@ def compare_outputs(o_gpu: np.ndarray, o_ref: np.ndarray, rows: Optional[np.ndar
     return mx, mean
 
 
-def compare_outputs_derived(o_gpu: np.ndarray, o_ref: np.ndarray, vmax: float):
-    """Output check for plain N(0, s^2) edge-case inputs, whose sharp rows push
-    |O| up to max|V|, beyond the video workloads the 2e-2 bound is stated for.
-    Bound per element:
+def compare_outputs_derived(o_gpu: np.ndarray, o_ref: np.ndarray, vmax: float, v_scale: float):
+    """Output check for inputs whose V is drawn at scale `v_scale` (N(0, v_scale^2))
+    and whose sharp rows push |O| up to max|V|, beyond the unit-scale video
+    workloads the 2e-2 / 2e-3 bounds are stated for. Bound per element:
     - the bf16 rounding of P (2^-9 relative, times max|V|);
     - plus the rounding of O (2^-9 relative);
-    - plus accumulation noise; each rounding term is taken twice for margin."""
+    - plus accumulation noise; each rounding term is taken twice for margin.
+    Every error term is relative to V's magnitude, so the mean-abs bound is the
+    stated 2e-3 times v_scale."""
     sel = ~np.isnan(o_ref)
     diff = np.abs(o_gpu[sel] - o_ref[sel])
     tol = 2.0 ** -8 * vmax + 2.0 ** -8 * np.abs(o_ref[sel]) + 1e-3
     assert np.all(np.isfinite(o_gpu[sel])), "non-finite GPU output"
     assert np.all(diff <= tol), f"output outside the derived bound: max-abs {diff.max():.3e}"
-    assert diff.mean() <= O_MEAN_ABS, f"mean-abs {diff.mean():.3e}"
+    assert diff.mean() <= O_MEAN_ABS * v_scale, f"mean-abs {diff.mean():.3e}"
     return float(diff.max()), float(diff.mean())
+
+
+# ---- full-size oracle fixtures (tests/golden/fullsize_*.npz) ---------------------------
+# Written by tests/golden/make_fullsize_fixtures.py, which calls only oracle/ and synth.
+GOLDEN = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "tests", "golden")
+
+
+def load_fixture(name: str) -> Dict[str, np.ndarray]:
+    with np.load(os.path.join(GOLDEN, f"fullsize_{name}.npz")) as z:
+        return {k: z[k] for k in z.files}
+
+
+def mask_workgroup_stats(mask: np.ndarray, cu, H: int, block: int) -> np.ndarray:
+    """[n_wg, 3] int64 per work-group (the library's row order: sequence, head,
+    Q-block): skipped tiles, sum of their indices j and of j^2, from a tile mask."""
+    rows = []
+    for b in range(len(cu) - 1):
+        n = osk.n_tiles(int(cu[b + 1] - cu[b]), block)
+        if n == 0:
+            continue
+        m = mask[b, :, :n, :n]
+        assert np.all(m != osk.TILE_NONE), "a visited tile is marked as absent"
+        sk = (m == osk.TILE_SKIPPED).astype(np.int64)
+        j = np.arange(n, dtype=np.int64)
+        rows.append(np.stack([sk.sum(-1), sk @ j, sk @ (j * j)], axis=-1).reshape(H * n, 3))
+    return np.concatenate(rows)
+
+
+def compare_workgroup_stats(stats: np.ndarray, fx: Dict[str, np.ndarray], col: int) -> Dict[str, int]:
+    """GPU per-work-group skip statistics against fixture column `col`.
+
+    A work-group with no tile in the decision band must match the oracle in
+    count, sum j and sum j^2 (its skip bits tile for tile, barring a
+    coincidence of all three sums); elsewhere the counts may differ by at most
+    the number of band tiles."""
+    band = fx["band"][:, col].astype(np.int64)
+    sc = list(fx["sum_cols"]).index(col)
+    want = np.stack([fx["count"][:, col], fx["sum_j"][:, sc], fx["sum_j2"][:, sc]], axis=-1).astype(np.int64)
+    assert stats.shape == want.shape, f"{stats.shape} work-groups vs the fixture's {want.shape}"
+    exact = band == 0
+    off = exact & np.any(stats != want, axis=1)
+    assert not off.any(), (f"{int(off.sum())} band-free work-groups differ from the oracle, e.g. row "
+                           f"{int(np.nonzero(off)[0][0])}: gpu {stats[off][0]} oracle {want[off][0]}")
+    diff = np.abs(stats[:, 0] - want[:, 0])
+    over = diff > band
+    assert not over.any(), f"count differs beyond the band at rows {np.nonzero(over)[0][:8]}"
+    return {"band_workgroups": int((~exact).sum()), "band_tiles": int(band.sum()), "flipped": int(diff.sum())}
+
+
+def compare_calibration_counts(counts: np.ndarray, tiles: np.ndarray, fx: Dict[str, np.ndarray],
+                               cols: Sequence[int]) -> Dict[str, int]:
+    """Calibration counts [n_wg, len(cols)] against the fixture columns: exact
+    where no tile of the work-group lies in the band, else within the band."""
+    np.testing.assert_array_equal(tiles, fx["tiles"])
+    band = fx["band"][:, cols].astype(np.int64)
+    want = fx["count"][:, cols].astype(np.int64)
+    diff = np.abs(np.asarray(counts, np.int64) - want)
+    assert np.all(diff[band == 0] == 0), f"{int((diff[band == 0] > 0).sum())} band-free counts differ"
+    assert np.all(diff <= band), "calibration counts differ beyond the band"
+    return {"band_tiles": int(band.sum()), "flipped": int(diff.sum()), "cells": int(diff.size)}
+
+
+def sampled_outputs_vs_oracle(x: Dict, cu, o: np.ndarray, mask: np.ndarray, t_bh: np.ndarray, block: int,
+                              qblocks: Sequence[Tuple[int, int, int]], sequential_every: int = 8):
+    """Outputs of the sampled Q-blocks against the oracle under the GPU's own
+    skip decisions (forced mask). Every `sequential_every`-th block runs the
+    oracle's tile loop; the others its fast form, which equals the loop under
+    any forced mask (pinned on the CPU). Returns (max-abs, mean-abs)."""
+    scale = osk.default_sm_scale(x["q"].shape[2])
+    worst, tot, n = 0.0, 0.0, 0
+    cache = {}
+    for idx, (b, h, i) in enumerate(qblocks):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        if (b, h) not in cache:
+            cache.clear()
+            cache[(b, h)] = (to_f64(x["k"][s0:s1, h]), to_f64(x["v"][s0:s1, h]))
+        kh, vh = cache[(b, h)]
+        r0, r1 = i * block, min(s1 - s0, (i + 1) * block)
+        qh = to_f64(x["q"][s0 + r0:s0 + r1, h])
+        nk = osk.n_tiles(s1 - s0, block)
+        forced = mask[b, h, i, :nk] == osk.TILE_SKIPPED
+        fn = osk.skip_softmax_qblock if idx % sequential_every == 0 else osk.skip_softmax_qblock_fast
+        ref = fn(qh, kh, vh, float(t_bh[b, h]), block, scale, forced_skip=forced)
+        diff = np.abs(o[s0 + r0:s0 + r1, h] - ref["o"])
+        assert np.all(np.isfinite(o[s0 + r0:s0 + r1, h])), f"non-finite output at {(b, h, i)}"
+        worst = max(worst, float(diff.max()))
+        tot += float(diff.sum())
+        n += diff.size
+    mean = tot / n
+    assert worst <= O_MAX_ABS and mean <= O_MEAN_ABS, f"output mismatch max {worst:.3e} mean {mean:.3e}"
+    return worst, mean
 
 
 def sample_qblocks(cu, H: int, block: int, heads: Sequence[int], per_head: int, seed: int):

@@ -12,8 +12,9 @@ from oracle import calibration as oc
 from oracle import skip_softmax as osk
 from synth import CONFIGS, make_inputs
 from synth.video_tokens import VideoTokenConfig
-from tests._parity import (compare_masks, compare_outputs, compare_outputs_derived, gpu_forward, log,
-                           sample_qblocks, t_matrix, to_device, to_f64)
+from tests._parity import (compare_calibration_counts, compare_masks, compare_outputs, compare_outputs_derived,
+                           compare_workgroup_stats, gpu_forward, load_fixture, log, mask_workgroup_stats,
+                           sample_qblocks, sampled_outputs_vs_oracle, t_matrix, to_device, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -155,6 +156,52 @@ def test_determinism():
         assert torch.equal(a, b)
 
 
+def _guarded(n, dtype, pad, fill):
+    """A device buffer of n elements with `pad` canary elements on each side."""
+    import torch
+    buf = torch.full((n + 2 * pad,), fill, dtype=dtype, device="cuda")
+    return buf, buf[pad:pad + n]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_canaries_around_counters_mask_and_calibration_outputs(causal):
+    """Every output the kernels write (skipped/total counters, the tile mask,
+    the output rows, calibration counts and tiles) sits between canary
+    regions; after the forward and the calibration pass the canaries are
+    unchanged, so no write lands outside the buffer the caller was asked for.
+    The ragged batch includes an empty sequence and a single partial tile."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    x, xd, cu = _inputs(RAGGED)
+    T, H, D = xd["q"].shape
+    B, blk = len(cu) - 1, RAGGED.block
+    prob, _ = ssa.make_problem(xd["q"], cu, blk)
+    nq, nk = ssa.tile_mask_dims(prob)
+    nwg = ssa.calib_num_workgroups(prob)
+    lams = np.geomspace(1e-6, 0.7, 16)
+    c64 = -0x21524111  # 0xDEADBEEF-like pattern in each canary
+    sk_buf, sk = _guarded(B * H, torch.int64, 8, c64)
+    tt_buf, tt = _guarded(B * H, torch.int64, 8, c64)
+    m_buf, m = _guarded(B * H * nq * nk, torch.uint8, 64, 0xA5)
+    o_buf, o = _guarded(T * H * D, torch.bfloat16, 64, 3.0)
+    c_buf, c = _guarded(nwg * lams.size, torch.int32, 16, c64)
+    t_buf, tl = _guarded(nwg, torch.int32, 16, c64)
+    ssa.attn_fwd(xd["q"], xd["k"], xd["v"], cu, 1e-2, block=blk, out=o.view(T, H, D), skipped=sk, total=tt,
+                 tile_mask=m.view(B, H, nq, nk), causal=causal)
+    ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, lams, block=blk, out=o.view(T, H, D),
+                       counts=c.view(nwg, lams.size), tiles=tl, causal=causal)
+    torch.cuda.synchronize()
+    for name, buf, pad, fill in (("skipped", sk_buf, 8, c64), ("total", tt_buf, 8, c64), ("mask", m_buf, 64, 0xA5),
+                                 ("out", o_buf, 64, 3.0), ("counts", c_buf, 16, c64), ("tiles", t_buf, 16, c64)):
+        head, tail = buf[:pad], buf[buf.numel() - pad:]
+        assert torch.all(head == fill) and torch.all(tail == fill), f"{name}: a canary was overwritten"
+    # and the guarded buffers hold real results: totals per head, tiles per work-group
+    nqs = [osk.n_tiles(int(cu[b + 1] - cu[b]), blk) for b in range(B)]
+    want = [n * (n + 1) // 2 if causal else n * n for n in nqs]
+    np.testing.assert_array_equal(tt.cpu().numpy().reshape(B, H), np.array([[w] * H for w in want]))
+    assert int(tl.sum()) == sum(w * H for w in want)
+
+
 @pytest.mark.parametrize("head_dim,block", [(64, 64), (128, 128)])
 def test_untouched_memory_outside_valid_rows(head_dim, block):
     """Output rows of other heads / padding stay untouched (strided layout with a gap)."""
@@ -232,28 +279,150 @@ def _sampled_parity(cfg, lams, heads, per_head, causal=False, kind="lambda", cou
     return fracs
 
 
-def test_wan5b_sampled_parity():
-    fr = _sampled_parity(CONFIGS["wan5b"], [0.0, 1e-3], heads=[0, 11, 23], per_head=3)
-    assert fr[0] == 0.0 and fr[1] > 0.0
+# ---- full-size parity against the oracle's fixtures ------------------------------------
+# tests/golden/fullsize_*.npz hold the oracle's per-work-group skip statistics
+# for whole configs (written by tests/golden/make_fullsize_fixtures.py from
+# oracle/ and synth only); the GPU runs the same configs at full size.
+def _check_dense(cu, H, blk, sk, tot, mask):
+    assert sk.sum() == 0
+    nqs = [osk.n_tiles(int(cu[b + 1] - cu[b]), blk) for b in range(len(cu) - 1)]
+    np.testing.assert_array_equal(tot, np.array([[n * n] * H for n in nqs]))
+    for b, n in enumerate(nqs):
+        assert np.all(mask[b, :, :n, :n] == osk.TILE_KEPT)
 
 
-def test_headline_sampled_parity():
-    fr = _sampled_parity(CONFIGS["headline"], [0.0, 8e-3], heads=[0, 19, 39], per_head=3)
-    assert fr[0] == 0.0 and fr[1] > 0.3
+def test_wan5b_full_tile_mask_and_per_head_counts():
+    """WAN-5B-like config (S=16,384, H=24) at lambda = 1e-3 and dense: the
+    whole tile mask against the oracle's (mismatches only inside the 1e-3
+    band), per-head skipped tiles reported and checked, and outputs of every
+    head (4 Q-blocks each, the last one included) against the oracle."""
+    cfg, fx = CONFIGS["wan5b"], load_fixture("wan5b")
+    x, xd, cu = _inputs(cfg)
+    H, blk = cfg.num_heads, cfg.block
+    n = osk.n_tiles(int(cu[1]), blk)
+    o0, sk0, tot0, m0 = gpu_forward(xd, cu, 0.0, "lambda", blk)
+    _check_dense(cu, H, blk, sk0, tot0, m0)
+    o, sk, tot, mask = gpu_forward(xd, cu, 1e-3, "lambda", blk)
+    skip = mask[0] == osk.TILE_SKIPPED
+    want = np.unpackbits(fx["skip_bits"])[:H * n * n].reshape(H, n, n).astype(bool)
+    band = np.unpackbits(fx["band_bits"])[:H * n * n].reshape(H, n, n).astype(bool)
+    hard = (skip != want) & ~band
+    assert not hard.any(), f"{int(hard.sum())} tiles differ outside the band, first at {np.argwhere(hard)[0]}"
+    per_head = skip.sum(axis=(1, 2))
+    np.testing.assert_array_equal(sk[0], per_head)
+    assert np.all(np.abs(per_head - fx["skip_per_head"]) <= band.sum(axis=(1, 2)))
+    log(f"  per-head skipped tiles of {n * n} (GPU / oracle):")
+    log("  " + " ".join(f"{h}:{int(a)}/{int(b)}" for h, (a, b) in enumerate(zip(per_head, fx["skip_per_head"]))))
+    log(f"  band tiles {int(band.sum())}, differing inside the band {int((skip != want).sum())}")
+    t = t_matrix(cu, H, 1e-3, "lambda")
+    qbs = sample_qblocks(cu, H, blk, range(H), 4, seed=cfg.seed)
+    mx, mean = sampled_outputs_vs_oracle(x, cu, o, mask, t, blk, qbs)
+    mx0, mean0 = sampled_outputs_vs_oracle(x, cu, o0, m0, t_matrix(cu, H, 0.0, "lambda"), blk, qbs[::4])
+    log(f"  outputs of {len(qbs)} Q-blocks: max-abs {mx:.2e} mean-abs {mean:.2e}; dense max-abs {mx0:.2e}")
+
+
+def test_headline_forward_matches_oracle_fixture():
+    """Headline config (S=75,600, H=40): at lambda = 8e-3 and lambda = 1 the
+    skip statistics of all 23,640 work-groups against the oracle's (exact
+    where no tile of a work-group lies in the 1e-3 band), per-head counts,
+    dense mode, and outputs of every head (4 Q-blocks each, the partial last
+    one included) against the oracle under the GPU's decisions."""
+    cfg, fx = CONFIGS["headline"], load_fixture("headline")
+    x, xd, cu = _inputs(cfg)
+    H, blk = cfg.num_heads, cfg.block
+    o0, sk0, tot0, m0 = gpu_forward(xd, cu, 0.0, "lambda", blk)
+    _check_dense(cu, H, blk, sk0, tot0, m0)
+    qbs = sample_qblocks(cu, H, blk, range(H), 4, seed=cfg.seed)
+    for col, lam in ((16, 8e-3), (17, 1.0)):
+        assert fx["column_value"][col] == lam
+        o, sk, tot, mask = gpu_forward(xd, cu, lam, "lambda", blk)
+        stats = mask_workgroup_stats(mask, cu, H, blk)
+        res = compare_workgroup_stats(stats, fx, col)
+        nq = osk.n_tiles(int(cu[1]), blk)
+        per_head_gpu = stats[:, 0].reshape(H, nq).sum(1)
+        per_head_ref = fx["count"][:, col].astype(np.int64).reshape(H, nq).sum(1)
+        band_head = fx["band"][:, col].astype(np.int64).reshape(H, nq).sum(1)
+        np.testing.assert_array_equal(sk[0], per_head_gpu)
+        assert np.all(np.abs(per_head_gpu - per_head_ref) <= band_head)
+        log(f"  lambda {lam}: sparsity {sk.sum() / tot.sum():.4f} (oracle {per_head_ref.sum() / tot.sum():.4f}); "
+            f"{res}")
+        if col == 16:
+            mx, mean = sampled_outputs_vs_oracle(x, cu, o, mask, t_matrix(cu, H, lam, "lambda"), blk, qbs)
+            log(f"  outputs of {len(qbs)} Q-blocks: max-abs {mx:.2e} mean-abs {mean:.2e}")
+    mx0, mean0 = sampled_outputs_vs_oracle(x, cu, o0, m0, t_matrix(cu, H, 0.0, "lambda"), blk, qbs[::4])
+    log(f"  dense outputs of {len(qbs[::4])} Q-blocks: max-abs {mx0:.2e} mean-abs {mean0:.2e}")
+
+
+@pytest.mark.parametrize("name", ["calib", "headline"])
+def test_headline_calibration_pass_matches_oracle_fixture(name):
+    """Calibration pass at the headline shape with 16 thresholds log-spaced over
+    [1e-6, 0.7] (the calibration config's own sample, and the headline sample):
+    every work-group's 16 counts against the oracle's (exact where no tile of
+    the work-group lies in the 1e-3 band), the fitted (a, b) through the C ABI
+    within 1e-3 relative of the oracle's fit of its own counts, and the
+    resolved lambdas for targets 0.25 / 0.5 / 0.7 against the oracle's resolve."""
+    import torch
+    import skip_softmax_video_amd as ssa
+    cfg, fx = CONFIGS[name], load_fixture(name)
+    x, xd, cu = _inputs(cfg)
+    lams = np.geomspace(1e-6, 0.7, 16)
+    np.testing.assert_array_equal(fx["column_value"][:16], lams)
+    o_cal, counts, tiles = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, lams, block=cfg.block)
+    torch.cuda.synchronize()
+    counts, tiles = counts.cpu().numpy(), tiles.cpu().numpy()
+    res = compare_calibration_counts(counts, tiles, fx, list(range(16)))
+    S = int(cu[1] - cu[0])
+    sp = ssa.calibration_sparsity(cu, cfg.num_heads, cfg.head_dim, cfg.block, counts, tiles)[0]
+    np.testing.assert_allclose(sp, fx["sparsity"], rtol=0, atol=res["band_tiles"] / tiles.sum() + 1e-15)
+    fit = ssa.calibration_fit(lams, sp, float(S))
+    assert fit.a == pytest.approx(float(fx["fit_a"]), rel=1e-3)
+    assert fit.b == pytest.approx(float(fx["fit_b"]), rel=1e-3)
+    assert fit.n_used == int(fx["fit_n_used"])
+    log(f"  [{name}] counts {res}; sparsity {np.round(sp, 4)}")
+    log(f"  fit a={fit.a:.6g} (oracle {float(fx['fit_a']):.6g}) b={fit.b:.6g} (oracle {float(fx['fit_b']):.6g})")
+    for tgt in (0.25, 0.5, 0.7):
+        st, lam, _ = ssa.resolve_threshold(S, target_sparsity=tgt, a=fit.a, b=fit.b, s_min=fit.s_min,
+                                           s_max=fit.s_max)
+        ref = oc.resolve_threshold(oc.ThresholdSpec(target_sparsity=tgt, a=float(fx["fit_a"]),
+                                                    b=float(fx["fit_b"]), s_min=float(fx["fit_s_min"]),
+                                                    s_max=float(fx["fit_s_max"])), S)
+        assert st == ref[0]
+        assert lam == pytest.approx(ref[1], rel=2e-3)  # a (1e-3) and exp(b t) (<= 1e-3 * |b t|)
+        log(f"  target {tgt}: lambda {lam:.6g} (oracle {ref[1]:.6g}) status {ssa.status_string(st)}")
 
 
 def test_varlen_full_size_per_head_scale_factor():
     """The varlen batch at full size (75,600 / 32,760 / 8,190 tokens, H=40):
     per-head scale factors with heads 0-1 forced dense, lambda_bh = sf_h / S_b.
-    sf = 650 puts lambda near 8.6e-3 on the longest sequence."""
-    cfg = CONFIGS["varlen"]
+    sf = 650 puts lambda near 8.6e-3 on the longest sequence. All 36,440
+    work-groups' skip statistics against the oracle's fixture, per-(sequence,
+    head) counts, and outputs of every head of every sequence (2 Q-blocks
+    each, the partial last ones included)."""
+    cfg, fx = CONFIGS["varlen"], load_fixture("varlen")
     sf = np.full(cfg.num_heads, 650.0)
     sf[:2] = 0.0
-    counts = []
-    fr = _sampled_parity(cfg, [sf], heads=[0, 1, 2, 23, 39], per_head=2, kind="scale_factor", counts_out=counts)
-    sk = counts[0]
-    assert sk[:, :2].sum() == 0 and np.all(sk[:, 2:].sum(axis=1) > 0)
-    assert fr[0] > 0.3
+    np.testing.assert_array_equal(fx["scale_factor"][0], sf)
+    x, xd, cu = _inputs(cfg)
+    H, blk = cfg.num_heads, cfg.block
+    o, sk, tot, mask = gpu_forward(xd, cu, sf, "scale_factor", blk)
+    stats = mask_workgroup_stats(mask, cu, H, blk)
+    res = compare_workgroup_stats(stats, fx, 0)
+    assert sk[:, :2].sum() == 0 and np.all(sk[:, 2:] > 0)
+    w = 0
+    for b in range(len(cu) - 1):
+        nq = osk.n_tiles(int(cu[b + 1] - cu[b]), blk)
+        ref_bh = fx["count"][w:w + H * nq, 0].astype(np.int64).reshape(H, nq).sum(1)
+        band_bh = fx["band"][w:w + H * nq, 0].astype(np.int64).reshape(H, nq).sum(1)
+        assert np.all(np.abs(sk[b] - ref_bh) <= band_bh)
+        np.testing.assert_array_equal(tot[b], np.full(H, nq * nq))
+        log(f"  sequence {b} (S={int(cu[b + 1] - cu[b])}): sparsity {sk[b].sum() / tot[b].sum():.4f} "
+            f"(oracle {ref_bh.sum() / tot[b].sum():.4f})")
+        w += H * nq
+    log(f"  {res}")
+    t = t_matrix(cu, H, sf, "scale_factor")
+    qbs = sample_qblocks(cu, H, blk, range(H), 2, seed=cfg.seed)
+    mx, mean = sampled_outputs_vs_oracle(x, cu, o, mask, t, blk, qbs)
+    log(f"  outputs of {len(qbs)} Q-blocks: max-abs {mx:.2e} mean-abs {mean:.2e}")
 
 
 def test_denoising_schedule_gating():
@@ -309,7 +478,7 @@ def test_pooled_calibration_multi_sample_multi_shape():
         _, counts, tiles = ssa.attn_calibrate(xd["q"], xd["k"], xd["v"], cu, lams, block=cfg.block)
         torch.cuda.synchronize()
         counts, tiles = counts.cpu().numpy(), tiles.cpu().numpy()
-        pool.add(cu, cfg.num_heads, cfg.block, counts, tiles)
+        pool.add(cu, cfg.num_heads, cfg.head_dim, cfg.block, counts, tiles)
         ref = osk.calibration_counts(xf["q"], xf["k"], xf["v"], cu, ts, cfg.block)
         ref_pool.add(ref["counts"], ref["tiles"], cu, cfg.num_heads, cfg.block)
         d = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, -math.inf, cfg.block, fast=True)["d"]
@@ -595,9 +764,10 @@ def test_launch_splitting_many_sequences_per_head_thresholds():
     ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk)
     band, mism = compare_masks(mask, ref, t, osk.workgroups(cu, H, blk))
     forced = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk, forced_mask=mask)
-    compare_outputs_derived(o, forced["o"], np.abs(xf["v"]).max())
+    mx, mean = compare_outputs(o, forced["o"])
     np.testing.assert_array_equal(tot, ref["total"])
     assert sk[:, 0].sum() == 0 and sk.sum() > 0
+    log(f"  output max-abs {mx:.3e} mean-abs {mean:.3e}")
     log(f"  skipped {sk.sum()}/{tot.sum()} band {band} band-mismatch {mism}")
 
 
@@ -615,13 +785,35 @@ def test_max_heads_and_tiny_sequences():
     ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk, fast=True)
     compare_masks(mask, ref, t, osk.workgroups(cu, H, blk))
     forced = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk, forced_mask=mask, fast=True)
-    compare_outputs_derived(o, forced["o"], np.abs(xf["v"]).max())
+    mx, mean = compare_outputs(o, forced["o"])
     np.testing.assert_array_equal(tot, ref["total"])
+    log(f"  output max-abs {mx:.3e} mean-abs {mean:.3e}")
     import skip_softmax_video_amd as ssa
     with pytest.raises(ssa.SSAError):
         x2 = make_random_inputs([8], 513, 64, seed=1)
         d2 = {n: to_device(x2[n]) for n in ("q", "k", "v")}
         ssa.attn_fwd(d2["q"], d2["k"], d2["v"], x2["cu_seqlens"], 0.1, block=64)
+
+
+def test_large_v_rounding_bound():
+    """Separate large-|V| case (V ~ N(0, 4^2), sharp rows): |O| reaches max|V|,
+    outside the range the 2e-2 bound is stated for, so the check is the bound
+    derived from the bf16 roundings of P and O (2^-8 max|V| + 2^-8 |O| + 1e-3
+    per element, mean-abs 2e-3 times V's scale)."""
+    from synth.video_tokens import make_random_inputs
+    lens = [1, 70, 129, 300]
+    H, D, blk = 8, 64, 64
+    x = make_random_inputs(lens, H, D, seed=24, scale=2.0, v_scale=4.0)
+    xd = {n: to_device(x[n]) for n in ("q", "k", "v")}
+    xf = {n: to_f64(x[n]) for n in ("q", "k", "v")}
+    cu = x["cu_seqlens"]
+    o, sk, tot, mask = gpu_forward(xd, cu, 0.25, "lambda", blk)
+    t = t_matrix(cu, H, 0.25, "lambda")
+    ref = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk)
+    compare_masks(mask, ref, t, osk.workgroups(cu, H, blk))
+    forced = osk.skip_softmax_forward(xf["q"], xf["k"], xf["v"], cu, t, blk, forced_mask=mask)
+    mx, mean = compare_outputs_derived(o, forced["o"], np.abs(xf["v"]).max(), v_scale=4.0)
+    log(f"  max|V| {np.abs(xf['v']).max():.2f} output max-abs {mx:.3e} mean-abs {mean:.3e}")
 
 
 @pytest.mark.parametrize("head_dim,block", [(64, 64), (64, 128), (128, 64)])
