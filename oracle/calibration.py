@@ -100,44 +100,35 @@ def fit_exponential_linear(lambdas: Sequence[float], sparsities: Sequence[float]
     It minimises sum_i (a e^{b s_i} - y_i)^2 with y_i = lambda_i * seq_k_i,
     over the same usable points as the log-space fit.
 
-    For a fixed b the best a is closed-form:
-        a(b) = sum y e^{bs} / sum e^{2bs}.
-    So the fit maximises H(b) = (sum y e^{bs})^2 / sum e^{2bs}. This is done
-    by a grid over b0 +- 100 in steps of 0.1 (b0 is the log-space slope), then
-    the root of dH/db inside the two cells around the best grid point, found
-    with scipy's brentq. Raises ValueError for degenerate data, or when the
-    maximiser lies at the edge of the grid.
+    Written as plain nonlinear least squares: scipy's Levenberg-Marquardt on
+    the residuals r_i = exp(ln a + b s_i) - y_i with their exact Jacobian,
+    parameterised by (ln a, b) so that a stays positive, started from the
+    log-space fit. Raises ValueError for fewer than two distinct usable
+    sparsities.
 
     Pinned by:
     - exact recovery of (a, b) from points on a known curve;
-    - the zero gradient of the squared error at the returned (a, b);
+    - the zero gradient of the squared error at the returned (a, b), and no
+      better neighbouring point;
     - scipy.optimize.curve_fit on noisy points (tests).
     """
-    from scipy.optimize import brentq
+    from scipy.optimize import least_squares
 
     x, y = _usable_points(lambdas, sparsities, seq_k)
     if x.size < 2 or np.unique(x).size < 2:
         raise ValueError("degenerate fit: fewer than two distinct usable sparsities")
-    b0 = fit_exponential_logspace(lambdas, sparsities, seq_k).b
-    xc = x - float(x.max())  # H is invariant to scaling u by e^{-b max(x)}
+    start = fit_exponential_logspace(lambdas, sparsities, seq_k)
 
-    def h(b):
-        u = np.exp(b * xc)
-        return np.sum(y * u) ** 2 / np.sum(u * u)
+    def residuals(p):
+        return np.exp(p[0] + p[1] * x) - y
 
-    def dh_sign(b):  # sign of dH/db: 2 N' D - N D' with N = sum y u, D = sum u^2
-        u = np.exp(b * xc)
-        n, d = np.sum(y * u), np.sum(u * u)
-        return 2.0 * np.sum(y * xc * u) * d - n * 2.0 * np.sum(xc * u * u)
+    def jacobian(p):
+        e = np.exp(p[0] + p[1] * x)
+        return np.stack([e, x * e], axis=1)
 
-    grid = b0 + np.linspace(-100.0, 100.0, 2001)
-    k = int(np.argmax([h(b) for b in grid]))
-    if k == 0 or k == grid.size - 1:
-        raise ValueError("degenerate fit: the linear-space optimum is not interior")
-    lo, hi = grid[k - 1], grid[k + 1]
-    b = float(brentq(dh_sign, lo, hi, xtol=1e-15, rtol=1e-15, maxiter=500))
-    u = np.exp(b * xc)
-    log_a = math.log(np.sum(y * u) / np.sum(u * u)) - b * float(x.max())
+    sol = least_squares(residuals, [start.log_a, start.b], jac=jacobian, method="lm",
+                        xtol=1e-15, ftol=1e-15, gtol=1e-15, max_nfev=20000)
+    log_a, b = float(sol.x[0]), float(sol.x[1])
     return Fit(a=math.exp(log_a), log_a=log_a, b=b, s_min=float(x.min()), s_max=float(x.max()),
                n_used=int(x.size))
 

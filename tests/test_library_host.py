@@ -285,8 +285,17 @@ def test_linear_fit_matches_oracle(seed):
     lam = np.minimum(a * np.exp(b * s) * np.exp(rng.normal(0, 0.25, n)) / seq_k, 1.0)
     got = ssa.calibration_fit(lam, s, seq_k, space="linear")
     ref = oc.fit_exponential_linear(lam, s, seq_k)
-    assert got.b == pytest.approx(ref.b, rel=1e-9)
-    assert got.a == pytest.approx(ref.a, rel=1e-9)
+    # The library searches b on a grid and bisects dH/db; the oracle runs plain
+    # Levenberg-Marquardt. Both must reach the same least-squares minimum. Along
+    # its flat direction the squared error changes only at the 1e-15 level, so
+    # the parameters agree to about 1e-7 while the minimum and the fitted
+    # values agree to rounding.
+    y = lam * seq_k
+    err = lambda f: np.sum((f.a * np.exp(f.b * s) - y) ** 2)
+    assert err(got) == pytest.approx(err(ref), rel=1e-12)
+    np.testing.assert_allclose(got.a * np.exp(got.b * s), ref.a * np.exp(ref.b * s), rtol=1e-7)
+    assert got.b == pytest.approx(ref.b, rel=1e-6)
+    assert got.a == pytest.approx(ref.a, rel=1e-6)
     assert (got.s_min, got.s_max, got.n_used) == (ref.s_min, ref.s_max, ref.n_used)
 
 
