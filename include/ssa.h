@@ -77,7 +77,10 @@ typedef struct ssa_problem {
   int32_t block;             /* Br = Bc in {64, 128}                              */
   const int32_t* cu_seqlens; /* HOST array [B + 1]: cu[0] = 0, non-decreasing;
                                 sequence b is tokens [cu[b], cu[b+1]); empty
-                                sequences are allowed                              */
+                                sequences are allowed. The library sees only the
+                                tensors' pointers, so cu[B] <= T (the rows the
+                                tensors hold) is the caller's duty; the Python
+                                binding checks it before any launch            */
   int64_t stride_token;      /* elements between tokens, same for q, k, v, o       */
   int64_t stride_head;       /* elements between heads, same for q, k, v, o        */
   double sm_scale;           /* softmax scale; 0 selects 1 / sqrt(D)               */
