@@ -46,7 +46,8 @@
 //     work-group is written at the end (no atomics).
 //   * V_j is fetched only when the vote kept the tile, issued right after
 //     the vote so that it lands while the softmax runs; K_{j+1} is fetched
-//     as soon as every wave is done reading K_j.
+//     into a second K buffer during S^T = K_j Q^T where LDS allows, else as
+//     soon as every wave is done reading K_j (see the tile loop).
 //   * Work-groups are remapped so that each XCD (8 per MI355X, 4 MB L2 each)
 //     receives a contiguous range of Q-blocks of the same head: co-resident
 //     work-groups stream the same K/V tiles through their XCD's L2.
@@ -120,15 +121,17 @@ __device__ __forceinline__ uint32_t head_extent(int rows, int64_t stride_tok) {
   return rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * stride_tok + D) * 2) : 0u;
 }
 
+// With di > 1 only instructions i0, i0 + di, ... are issued, so a tile fetch
+// can be spread over the steps of a product.
 template <int D, int BLK, bool IS_V>
 __device__ __forceinline__ void dma_load(const uint16_t* head, uint32_t bytes, uint16_t* lds, int row0,
-                                         int64_t stride_tok, int wave, int lane) {
+                                         int64_t stride_tok, int wave, int lane, int i0 = 0, int di = 1) {
   using SH = Shape<D, BLK>;
   constexpr int RPI = 64 / SH::CH;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)head, 0, bytes, kBufferFlags);
   const int lrow = lane / SH::CH;
 #pragma unroll
-  for (int i = 0; i < SH::DMA; ++i) {
+  for (int i = i0; i < SH::DMA; i += di) {
     const int rin = RPI * (i * SH::NW + wave);  // first row of this instruction within the tile
     const int row = rin + lrow;
     const int chunk = (lane % SH::CH) ^ (IS_V ? swz_v<SH::CH>(row) : swz_k<SH::CH>(row));
@@ -256,13 +259,13 @@ __device__ __forceinline__ int swz_v8(int row) {
 // global -> LDS copy of one BLK x D e4m3 tile (same scheme as dma_load).
 template <int D, int BLK, bool IS_V>
 __device__ __forceinline__ void dma_load8(const uint8_t* head, uint32_t bytes, uint8_t* lds, int row0,
-                                          int64_t stride_tok, int wave, int lane) {
+                                          int64_t stride_tok, int wave, int lane, int i0 = 0, int di = 1) {
   using SH = Shape8<D, BLK>;
   constexpr int RPI = 64 / SH::CH;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)head, 0, bytes, kBufferFlags);
   const int lrow = lane / SH::CH;
 #pragma unroll
-  for (int i = 0; i < SH::DMA; ++i) {
+  for (int i = i0; i < SH::DMA; i += di) {
     const int rin = RPI * (i * SH::NW + wave);
     const int row = rin + lrow;
     const int chunk = (lane % SH::CH) ^ (IS_V ? swz_v8<SH::CH>(row) : swz_k8<SH::CH>(row));
@@ -350,7 +353,12 @@ __device__ __forceinline__ uint32_t load_scale_row(__amdgpu_buffer_rsrc_t rsrc, 
 // multiplied, and that lives in these classes:
 //   Qk*: the Q fragment (loaded once), the K tile fetch (with its per-lane
 //        block scales in the MX mode) and S^T = K_j Q^T into 4 accumulator
-//        blocks of 32 keys;
+//        blocks of 32 keys. scores() takes a hook that it calls once per d
+//        step, before that step's MFMAs; fetch_part(.., s, on) is the share
+//        of a tile fetch that goes with step s, so the next K tile can stream
+//        in during this one (with on = false its loads have an empty range:
+//        they touch no memory and leave zeros, which keeps the loop free of
+//        branches around them);
 //   Pv*: the V tile fetch, the softmax numerator P (exponentials, the row
 //        sum and the rounding to the P.V operand type) and O^T += V_j^T P^T.
 // ===========================================================================
@@ -378,7 +386,13 @@ struct QkBf16 {
   __device__ void fetch(uint8_t* lds, int j, int wave, int lane) {
     dma_load<D, BLK, false>(kbase, bytes, reinterpret_cast<uint16_t*>(lds), j * BLK, stride, wave, lane);
   }
-  __device__ void scores(floatx16 (&sc)[SH::KB], const uint8_t* lds, int l32, int hl) const {
+  __device__ void fetch_part(uint8_t* lds, int j, int wave, int lane, int s, bool on) {
+    dma_load<D, BLK, false>(kbase, on ? bytes : 0u, reinterpret_cast<uint16_t*>(lds), j * BLK, stride, wave, lane, s,
+                            SH::DS);
+  }
+  __device__ void advance() {}
+  template <class Hook>
+  __device__ void scores(floatx16 (&sc)[SH::KB], const uint8_t* lds, int l32, int hl, Hook&& hook) const {
     const uint16_t* k_lds = reinterpret_cast<const uint16_t*>(lds);
 #pragma unroll
     for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
@@ -387,6 +401,7 @@ struct QkBf16 {
     for (int kb = 0; kb < SH::KB; ++kb) ka[0][kb] = read_k<SH>(k_lds, kb, 0, l32, hl);
 #pragma unroll
     for (int s = 0; s < SH::DS; ++s) {
+      hook(s);
       if (s + 1 < SH::DS) {
 #pragma unroll
         for (int kb = 0; kb < SH::KB; ++kb) ka[(s + 1) & 1][kb] = read_k<SH>(k_lds, kb, s + 1, l32, hl);
@@ -429,11 +444,17 @@ struct QkFp8 {
   __device__ void fetch(uint8_t* lds, int j, int wave, int lane) {
     dma_load8<D, BLK, false>(kbase, bytes, lds, j * BLK, stride, wave, lane);
   }
-  __device__ void scores(floatx16 (&sc)[SH::KB], const uint8_t* k_lds, int l32, int hl) const {
+  __device__ void fetch_part(uint8_t* lds, int j, int wave, int lane, int s, bool on) {
+    dma_load8<D, BLK, false>(kbase, on ? bytes : 0u, lds, j * BLK, stride, wave, lane, s, SH::DS);
+  }
+  __device__ void advance() {}
+  template <class Hook>
+  __device__ void scores(floatx16 (&sc)[SH::KB], const uint8_t* k_lds, int l32, int hl, Hook&& hook) const {
 #pragma unroll
     for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
 #pragma unroll
     for (int s = 0; s < SH::DS; ++s) {
+      hook(s);
       intx8 ka[SH::KB];
 #pragma unroll
       for (int kb = 0; kb < SH::KB; ++kb) ka[kb] = read_k8<SH>(k_lds, kb, s, l32, hl);
@@ -454,11 +475,12 @@ struct QkMx {
   const uint8_t* kbase;
   uint32_t bytes;
   int64_t stride;
-  __amdgpu_buffer_rsrc_t ks_rsrc;
+  __amdgpu_buffer_rsrc_t ks_rsrc, ks_rsrc_off;  // K scale rows; the same with an empty range
   uint32_t sc_lane, sc_blk, sc_tile;
   intx8 qf[SH::DS];
   uint32_t qsc[SH::DS];
-  uint32_t ks[SH::KB];  // scale rows of this lane's keys in the K tile being fetched / used
+  uint32_t ks[SH::KB];     // scale rows of this lane's keys in the K tile in use
+  uint32_t ks_nx[SH::KB];  // the same for the next tile when it is fetched during this one
 
   __device__ QkMx(const LaunchParams& p, const WorkItem& w, int64_t head_off, int qrow, bool qvalid, int hl)
       : kbase(reinterpret_cast<const uint8_t*>(p.k) + head_off), bytes(head_extent8<D>(w.S, p.stride_tok)),
@@ -467,6 +489,7 @@ struct QkMx {
     const int64_t sc_off = (int64_t)w.tok0 * p.bs_tok + (int64_t)w.h * p.bs_head;
     const uint32_t sc_bytes = w.S > 0 ? (uint32_t)((int64_t)(w.S - 1) * p.bs_tok + SROW) : 0u;
     ks_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_bscale + sc_off), 0, sc_bytes, kBufferFlags);
+    ks_rsrc_off = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_bscale + sc_off), 0, 0u, kBufferFlags);
     const __amdgpu_buffer_rsrc_t qs_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.q_bscale + sc_off), 0, sc_bytes, kBufferFlags);
     // lane: key 32 kb + l32 (the host keeps (S + BLK) * bs_tok within 32 bits)
@@ -496,11 +519,26 @@ struct QkMx {
 #pragma unroll
     for (int kb = 0; kb < SH::KB; ++kb) ks[kb] = load_scale_row<D>(ks_rsrc, sc_lane, j * sc_tile + kb * sc_blk);
   }
-  __device__ void scores(floatx16 (&sc)[SH::KB], const uint8_t* k_lds, int l32, int hl) const {
+  // the scale rows go with step 0; advance() makes them current once S^T of this tile is done
+  __device__ void fetch_part(uint8_t* lds, int j, int wave, int lane, int s, bool on) {
+    dma_load8<D, BLK, false>(kbase, on ? bytes : 0u, lds, j * BLK, stride, wave, lane, s, SH::DS);
+    if (s == 0) {
+      const __amdgpu_buffer_rsrc_t r = on ? ks_rsrc : ks_rsrc_off;
+#pragma unroll
+      for (int kb = 0; kb < SH::KB; ++kb) ks_nx[kb] = load_scale_row<D>(r, sc_lane, j * sc_tile + kb * sc_blk);
+    }
+  }
+  __device__ void advance() {
+#pragma unroll
+    for (int kb = 0; kb < SH::KB; ++kb) ks[kb] = ks_nx[kb];
+  }
+  template <class Hook>
+  __device__ void scores(floatx16 (&sc)[SH::KB], const uint8_t* k_lds, int l32, int hl, Hook&& hook) const {
 #pragma unroll
     for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
 #pragma unroll
     for (int s = 0; s < SH::DS; ++s) {
+      hook(s);
       intx8 ka[SH::KB];
 #pragma unroll
       for (int kb = 0; kb < SH::KB; ++kb) ka[kb] = read_k8_mx<SH>(k_lds, kb, s, l32, hl);
@@ -636,13 +674,35 @@ struct PvFp8 {
 
 // ===========================================================================
 // The tile loop (forward and calibration), one work-group per Q-block.
+//
+// Two buffering schemes for K, chosen by LDS size (two work-groups share a
+// CU's 160 KB):
+//   * double K, when two K tiles and one V tile fit in 64 KB (every e4m3 and
+//     block-scaled shape, bf16 with head_dim 64 or 64-row tiles) and the
+//     kernel skips tiles (not the calibration pass): K_{j+1} is issued into
+//     the other K buffer at the start of S^T = K_j Q^T. A skipped tile then
+//     costs its product, the vote and one barrier (every wave voted to skip
+//     and waited for its share of K_{j+1} before it); a kept tile adds the V
+//     fetch and a second barrier before P.V, after which both tiles are in.
+//   * single K otherwise (bf16 with head_dim 128 and 128-row tiles, where K
+//     and V take 32 KB each): K_{j+1} is fetched after the vote, once every
+//     wave is done reading K_j, and every tile ends with a wait and a barrier.
 // ===========================================================================
+template <class QK, class PV, bool CALIB>
+struct Buffering {
+  static constexpr bool kDoubleK = !CALIB && 2 * QK::LDS_BYTES + PV::LDS_BYTES <= 64 * 1024;
+  static constexpr int K1_BYTES = kDoubleK ? QK::LDS_BYTES : 16;  // unused in the single-K scheme
+  static constexpr int K1_ALIGN = kDoubleK ? 1024 : 16;
+};
+
 template <int D, int BLK, class QK, class PV, bool CALIB>
 __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {  // 2*BLK = 64 * BLK / 32 threads
   constexpr int NW = BLK / 32;  // waves, 32 query rows each
   constexpr int KB = BLK / 32;  // 32-key blocks of S^T
   constexpr int MB = D / 32;    // 32-wide d blocks of O^T
+  constexpr bool kDoubleK = Buffering<QK, PV, CALIB>::kDoubleK;
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds[QK::LDS_BYTES];
+  __shared__ alignas(Buffering<QK, PV, CALIB>::K1_ALIGN) uint8_t k_lds1[Buffering<QK, PV, CALIB>::K1_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds[PV::LDS_BYTES];
   __shared__ uint64_t vote[NW];
   __shared__ float dvote[NW];  // calibration: each wave's maximum of x
@@ -681,12 +741,19 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
   wait_dma();
   __syncthreads();
 
-  for (int j = 0; j < nK; ++j) {
+  // One tile. kcur holds K_j; in the double-K scheme K_{j+1} goes to knext.
+  // Both are always the named LDS arrays (the loop below is unrolled by two
+  // in that scheme), so the compiler sees that the reads of kcur do not
+  // depend on the copy into knext and adds no wait for it.
+  auto tile = [&](uint8_t* kcur, uint8_t* knext, const int j) __attribute__((always_inline)) {
     const int nvalid = min(BLK, S - j * BLK);
 
     // ---- S^T = K_j Q^T (always paid) -------------------------------------
     floatx16 sc[KB];
-    qk.scores(sc, k_lds, l32, hl);
+    qk.scores(sc, kcur, l32, hl, [&](int s) __attribute__((always_inline)) {
+      if constexpr (kDoubleK) qk.fetch_part(knext, j + 1, wave, lane, s, j + 1 < nK);
+    });
+    if constexpr (kDoubleK) qk.advance();
     // keys past the sequence end; causal: keys after this lane's query (diagonal tile)
     const int kmax = (p.causal && j == qb) ? min(nvalid, wave * 32 + l32 + 1) : nvalid;
     if (p.causal ? j == qb : nvalid < BLK) {
@@ -708,6 +775,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
     float rowmax, x;
     tile_margin(xhalf_max(mx), c2, m_true, rowmax, x);  // m_true = -inf gives x = +inf
     if (!qvalid) x = -INFINITY;
+    bool wait_k = false;
     if constexpr (CALIB) {
       // d = max over valid rows; "some row has x >= t_k" is exactly d >= t_k
       const float dw = wave_max(x);
@@ -715,8 +783,13 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
     } else {
       const bool kw = wave_any(x >= t);
       if (lane == 0) vote[wave] = kw ? 1ull : 0ull;
+      // A wave that keeps the tile knows it is kept and waits for its share of
+      // K_{j+1} with V_j, before the second barrier. The others wait now, so
+      // that when every wave skips, K_{j+1} is complete at this barrier.
+      wait_k = kDoubleK && !kw;
     }
-    __syncthreads();  // votes visible; every wave is done reading K_j and V_{j-1}
+    if (wait_k) wait_dma();
+    __syncthreads();  // votes (and K_{j+1}) visible; every wave is done reading K_j and V_{j-1}
 
     bool keep;
     if constexpr (CALIB) {
@@ -735,7 +808,7 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
         p.tile_mask[((int64_t)((p.seq_abs0 + b) * H + h) * p.mask_nq + qb) * p.mask_nk + j] = keep ? 0 : 1;
     }
 
-    if (j + 1 < nK) qk.fetch(k_lds, j + 1, wave, lane);
+    if (!kDoubleK && j + 1 < nK) qk.fetch(kcur, j + 1, wave, lane);
     typename PV::PFrag pb;
     if (keep) {
       pv.fetch(v_lds, j, wave, lane);
@@ -752,11 +825,22 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
       }
       PV::make_p(sc, c2, -m_use, l, pb);
     }
-    wait_dma();
-    __syncthreads();  // K_{j+1} (and its scales) and V_j visible
+    if (!kDoubleK || keep) {
+      wait_dma();
+      __syncthreads();  // V_j (and in the single-K scheme K_{j+1} with its scales) visible
+    }
 
     // ---- O^T += V_j^T P^T ------------------------------------------------
     if (keep) pv.accumulate(acc, v_lds, pb);
+  };
+
+  if constexpr (kDoubleK) {
+    for (int j = 0; j < nK; j += 2) {
+      tile(k_lds, k_lds1, j);
+      if (j + 1 < nK) tile(k_lds1, k_lds, j + 1);
+    }
+  } else {
+    for (int j = 0; j < nK; ++j) tile(k_lds, k_lds, j);
   }
 
   // ---- epilogue ---------------------------------------------------------
