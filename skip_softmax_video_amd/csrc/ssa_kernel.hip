@@ -15,19 +15,23 @@
 //     query rows. D = head dim. Two work-groups share a CU (<= 256 VGPRs +
 //     AGPRs per wave, 64 KB of LDS per work-group), so each SIMD runs two
 //     waves that hide each other's LDS, barrier and memory latency.
-//   * Scores are computed transposed, S^T = K_j Q^T, with
-//     v_mfma_f32_32x32x16_bf16: lane l then holds query (l % 32) and 16 keys
-//     per 32-key block, so the per-row max and sum are in-register
-//     reductions plus one v_permlane32_swap with lane l ^ 32.
-//   * The same registers, rounded to bf16, are the B operand of
-//     O^T += V_j^T P^T; V_j^T is read from the row-major V tile in LDS with
-//     ds_read_b64_tr_b16 (4x16 transposing read). The per-lane key order
-//     inside a 16-key MFMA step is permuted identically on both operands.
-//   * O^T accumulates in registers; lane l owns query (l % 32), so the
-//     rescale factor and row sum are per-lane scalars. The accumulator is
-//     rescaled lazily: the exponent base only moves when some row's maximum
-//     rose by more than 2^8, which keeps P <= 256 and the result unchanged
-//     up to rounding.
+//   * Scores are computed transposed, S^T = K_j Q^T, so that each lane holds
+//     whole query rows' worth of keys and the per-row max and sum are
+//     in-register reductions plus cross-lane swaps. bf16 uses
+//     v_mfma_f32_16x16x32_bf16 (lane l holds queries l % 16 and 16 + l % 16,
+//     4 keys of every 16-key block; partners in lanes l ^ 16, ^ 32, ^ 48),
+//     which does the work of the 32x32x16 shape for less energy per FLOP.
+//     The e4m3 and block-scaled modes use the 32x32x64 scaled MFMA (lane l
+//     holds query l % 32, 16 keys per 32-key block; partner lane l ^ 32).
+//   * The same registers, rounded to the P.V operand type, are the B
+//     operand of O^T += V_j^T P^T; V_j^T is read from the row-major V tile
+//     in LDS with transposing reads (ds_read_b64_tr_b16 / _b8). The per-lane
+//     key order inside a P.V step is permuted identically on both operands.
+//   * O^T accumulates in registers with each lane owning the same query rows
+//     as in the scores, so the rescale factors and row sums are per-lane
+//     values. The accumulator is rescaled lazily: the exponent base only
+//     moves when some row's maximum rose by more than 2^8, which keeps
+//     P <= 256 and the result unchanged up to rounding.
 //   * K and V tiles go global -> LDS with buffer_load_dwordx4 ... lds (no
 //     register staging). Each wave instruction fills 1 KB of LDS; the
 //     16-byte granules of a row are XOR-swizzled so that the MFMA operand
@@ -36,9 +40,9 @@
 //     descriptor's range and read as zero: their scores are masked to -inf
 //     and their P is 0.
 //   * Skip vote: every lane forms x = rowmax * sm_scale * log2(e) - m for its
-//     query (m = running max before the tile; -inf on the first tile, so x =
-//     +inf and the first tile is always kept). A wave keeps the tile if any
-//     valid lane has x >= t (one ballot); the work-group ORs the waves'
+//     queries (m = running max before the tile; -inf on the first tile, so
+//     x = +inf and the first tile is always kept). A wave keeps the tile if
+//     any valid row has x >= t (one ballot); the work-group ORs the waves'
 //     flags through LDS, so d = max_r x_r < t exactly when nobody keeps.
 //     The calibration instantiation never skips: each wave reduces x to its
 //     maximum (DPP), the work-group takes d = the maximum over waves, and
@@ -106,6 +110,22 @@ __device__ __forceinline__ int swz_v(int row) {
   }
 }
 
+// XOR swizzle of a V row read by the 16x16 layout's transposing reads: 8
+// consecutive rows x 2 granules per 32 lanes (4 rows per 16 lanes) land on
+// distinct bank groups for 32- and 64-bank LDS (head_dim 128; head_dim 64
+// rows are 128 bytes, where 4 consecutive rows are kept apart).
+template <int CH>
+__device__ __forceinline__ int swz_v16(int row) {
+  if constexpr (CH == 16) {
+    return 2 * (row & 7);
+  } else {
+    return 2 * (row & 3);
+  }
+}
+
+// Which swizzle a tile copy applies.
+enum class Swz { K, V, V16 };
+
 // global -> LDS copy of one BLK x D tile with buffer_load_dwordx4 ... lds.
 // The buffer descriptor covers exactly the head's valid rows (base = the
 // head's first row, `bytes` = extent of rows [0, S)), so rows past the end of
@@ -123,19 +143,27 @@ __device__ __forceinline__ uint32_t head_extent(int rows, int64_t stride_tok) {
 
 // With di > 1 only instructions i0, i0 + di, ... are issued, so a tile fetch
 // can be spread over the steps of a product.
-template <int D, int BLK, bool IS_V>
+template <int D, int BLK, Swz SW>
 __device__ __forceinline__ void dma_load(const uint16_t* head, uint32_t bytes, uint16_t* lds, int row0,
                                          int64_t stride_tok, int wave, int lane, int i0 = 0, int di = 1) {
   using SH = Shape<D, BLK>;
   constexpr int RPI = 64 / SH::CH;
+  // rows repeat their swizzle with this period
+  constexpr int PERIOD = SW == Swz::K ? SH::CH : SW == Swz::V ? 4 : (SH::CH == 16 ? 8 : 4);
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)head, 0, bytes, kBufferFlags);
   const int lrow = lane / SH::CH;
+  auto lane_off = [&](int row) {
+    const int sw = SW == Swz::K ? swz_k<SH::CH>(row) : SW == Swz::V ? swz_v<SH::CH>(row) : swz_v16<SH::CH>(row);
+    const int chunk = (lane % SH::CH) ^ sw;
+    return (uint32_t)(((int64_t)lrow * stride_tok + chunk * 8) * 2);
+  };
+  // When consecutive instructions advance by whole swizzle periods (the usual
+  // case) every instruction has the same per-lane offset: compute it once.
+  const uint32_t voff0 = lane_off(RPI * wave + lrow);
 #pragma unroll
   for (int i = i0; i < SH::DMA; i += di) {
     const int rin = RPI * (i * SH::NW + wave);  // first row of this instruction within the tile
-    const int row = rin + lrow;
-    const int chunk = (lane % SH::CH) ^ (IS_V ? swz_v<SH::CH>(row) : swz_k<SH::CH>(row));
-    const uint32_t voff = (uint32_t)(((int64_t)lrow * stride_tok + chunk * 8) * 2);
+    const uint32_t voff = (RPI * SH::NW) % PERIOD == 0 ? voff0 : lane_off(rin + lrow);
     const uint32_t soff = (uint32_t)((int64_t)(row0 + rin) * stride_tok * 2);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + (i * SH::NW + wave) * 512), 16, voff, soff, 0,
                                              0);
@@ -155,13 +183,41 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// the same with the partner in lane l ^ 16
+__device__ __forceinline__ float xrow_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xrow_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-// A operand of S^T = K Q^T for key block kb, d step s: K[32 kb + l32][16 s + 8 hl .. + 7]
+// A operand of the 16x16x32 S^T = K Q^T for 16-key block kb, 32-wide d
+// step s: K[16 kb + l16][32 s + 8 lq .. + 7] (l16 = l % 16, lq = l / 16)
 template <class SH>
-__device__ __forceinline__ bf16x8 read_k(const uint16_t* k_lds, int kb, int s, int l32, int hl) {
-  const int row = 32 * kb + l32;
-  const int gran = row * SH::CH + ((2 * s + hl) ^ swz_k<SH::CH>(row));
+__device__ __forceinline__ bf16x8 read_k16(const uint16_t* k_lds, int kb, int s, int l16, int lq) {
+  const int row = 16 * kb + l16;
+  const int gran = row * SH::CH + ((4 * s + lq) ^ swz_k<SH::CH>(row));
   return *reinterpret_cast<const bf16x8*>(k_lds + gran * 8);
+}
+
+// A operand of the 16x16x32 O^T += V^T P^T for 32-key step ks, 16-wide d
+// block mb: lane l gets column d = 16 mb + l16 at keys 32 ks + 4 lq + (0..3)
+// (slots 0-3) and 32 ks + 16 + 4 lq + (0..3) (slots 4-7), the key order of
+// P's slots. Each transposing read covers 4 rows x 16 columns per 16 lanes:
+// source lane i names row i / 4 and columns 4 (i % 4) .. + 3, and lane j
+// receives column j; voff holds this lane's row-in-group and column part.
+template <class SH>
+__device__ __forceinline__ bf16x8 read_vt16(const uint16_t* v_lds, int ks, int mb, int tr_row, int tr_col) {
+  const int r_lo = 32 * ks + tr_row;
+  const int r_hi = r_lo + 16;
+  const int c = 16 * mb + tr_col;  // element column, a multiple of 4
+  const uint16_t* lo = v_lds + (r_lo * SH::CH + ((c >> 3) ^ swz_v16<SH::CH>(r_lo))) * 8 + (c & 7);
+  const uint16_t* hi = v_lds + (r_hi * SH::CH + ((c >> 3) ^ swz_v16<SH::CH>(r_hi))) * 8 + (c & 7);
+  const shortx4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)lo);
+  const shortx4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)hi);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // A operand of O^T += V^T P^T for 16-key step s, d block mb: two transposing
@@ -348,9 +404,80 @@ __device__ __forceinline__ uint32_t load_scale_row(__amdgpu_buffer_rsrc_t rsrc, 
 }
 
 // ===========================================================================
+// Score layouts. After S^T = K_j Q^T each lane holds some of the wave's 32
+// query rows and, for each, some of the tile's keys; the tile loop reaches
+// the scores only through these descriptions.
+//   L32 (32x32 MFMA results): lane l holds query l % 32; register r of
+//       32-key block kb is key 32 kb + 8 (r / 4) + 4 (l / 32) + r % 4. The
+//       rest of the row is in lane l ^ 32.
+//   L16 (16x16 MFMA results): lane l holds queries l % 16 and 16 + l % 16
+//       (rows i = 0, 1); register r of 16-key block kb is key
+//       16 kb + 4 (l / 16) + r. Each row is spread over lanes l, l ^ 16,
+//       l ^ 32 and l ^ 48.
+// ===========================================================================
+template <int BLK>
+struct L32 {
+  static constexpr int NR = 1;  // query rows per lane
+  using Scores = floatx16[BLK / 32];
+  __device__ static int row(int, int lane) { return lane & 31; }
+  __device__ static void mask(Scores& sc, int lane, const int (&kmax)[NR]) {
+#pragma unroll
+    for (int kb = 0; kb < BLK / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (key >= kmax[0]) sc[kb][r] = -INFINITY;
+      }
+  }
+  // the tile's maximum of each row, in every lane holding it
+  __device__ static void row_max(const Scores& sc, float (&mx)[NR]) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < BLK / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[kb][r]);
+    mx[0] = xhalf_max(m);
+  }
+  // total of a per-lane partial over the row's lanes
+  __device__ static float row_sum(float x) { return xhalf_sum(x); }
+};
+
+template <int BLK>
+struct L16 {
+  static constexpr int NR = 2;
+  static constexpr int KB = BLK / 16;  // 16-key blocks
+  using Scores = floatx4[NR][KB];
+  __device__ static int row(int i, int lane) { return 16 * i + (lane & 15); }
+  __device__ static void mask(Scores& sc, int lane, const int (&kmax)[NR]) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 16 * kb + 4 * (lane >> 4) + r;
+          if (key >= kmax[i]) sc[i][kb][r] = -INFINITY;
+        }
+  }
+  __device__ static void row_max(const Scores& sc, float (&mx)[NR]) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, sc[i][kb][r]);
+      mx[i] = xhalf_max(xrow_max(m));
+    }
+  }
+  __device__ static float row_sum(float x) { return xhalf_sum(xrow_sum(x)); }
+};
+
+// ===========================================================================
 // Operand policies. The tile loop below is written once; what differs between
 // the bf16, e4m3 and block-scaled q/k modes is how Q, K and V are held and
-// multiplied, and that lives in these classes:
+// multiplied, and that lives in these classes (each names its score layout;
+// a QK and a PV policy that work together share it):
 //   Qk*: the Q fragment (loaded once), the K tile fetch (with its per-lane
 //        block scales in the MX mode) and S^T = K_j Q^T into 4 accumulator
 //        blocks of 32 keys. scores() takes a hook that it calls once per d
@@ -363,52 +490,66 @@ __device__ __forceinline__ uint32_t load_scale_row(__amdgpu_buffer_rsrc_t rsrc, 
 //        sum and the rounding to the P.V operand type) and O^T += V_j^T P^T.
 // ===========================================================================
 
-// bf16 Q and K: v_mfma_f32_32x32x16_bf16 with the K operand read one d step ahead.
+// bf16 Q and K: v_mfma_f32_16x16x32_bf16 (layout L16). A K fragment is read
+// one d step ahead of its MFMAs and feeds both of the lane's query rows.
+// (The 16x16 shape does the same work as 32x32x16 for less energy per FLOP;
+// at the part's power limit that is what the bf16 kernel runs at.)
 template <int D, int BLK>
 struct QkBf16 {
   using SH = Shape<D, BLK>;
+  using Layout = L16<BLK>;
+  static constexpr int NR = Layout::NR;
+  static constexpr int KB = Layout::KB;
+  static constexpr int DS = D / 32;  // 32-wide d steps
   static constexpr int LDS_BYTES = BLK * D * 2;
   const uint16_t* kbase;
   uint32_t bytes;
   int64_t stride;
-  bf16x8 qf[SH::DS];
+  bf16x8 qf[NR][DS];  // B operand: query row i, d [32 s + 8 (l / 16), + 8)
 
-  __device__ QkBf16(const LaunchParams& p, const WorkItem& w, int64_t head_off, int qrow, bool qvalid, int hl)
+  __device__ QkBf16(const LaunchParams& p, const WorkItem& w, int64_t head_off, const int (&qrow)[NR],
+                    const bool (&qvalid)[NR], int lane)
       : kbase(p.k + head_off), bytes(head_extent<D>(w.S, p.stride_tok)), stride(p.stride_tok) {
-    const uint16_t* qp = p.q + head_off + (int64_t)(qvalid ? qrow : 0) * p.stride_tok + 8 * hl;
 #pragma unroll
-    for (int s = 0; s < SH::DS; ++s) {
-      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-      if (qvalid) raw = *reinterpret_cast<const uint4*>(qp + 16 * s);
-      qf[s] = __builtin_bit_cast(bf16x8, raw);
+    for (int i = 0; i < NR; ++i) {
+      const uint16_t* qp = p.q + head_off + (int64_t)(qvalid[i] ? qrow[i] : 0) * p.stride_tok + 8 * (lane >> 4);
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+        if (qvalid[i]) raw = *reinterpret_cast<const uint4*>(qp + 32 * s);
+        qf[i][s] = __builtin_bit_cast(bf16x8, raw);
+      }
     }
   }
   __device__ void fetch(uint8_t* lds, int j, int wave, int lane) {
-    dma_load<D, BLK, false>(kbase, bytes, reinterpret_cast<uint16_t*>(lds), j * BLK, stride, wave, lane);
+    dma_load<D, BLK, Swz::K>(kbase, bytes, reinterpret_cast<uint16_t*>(lds), j * BLK, stride, wave, lane);
   }
   __device__ void fetch_part(uint8_t* lds, int j, int wave, int lane, int s, bool on) {
-    dma_load<D, BLK, false>(kbase, on ? bytes : 0u, reinterpret_cast<uint16_t*>(lds), j * BLK, stride, wave, lane, s,
-                            SH::DS);
+    dma_load<D, BLK, Swz::K>(kbase, on ? bytes : 0u, reinterpret_cast<uint16_t*>(lds), j * BLK, stride, wave, lane,
+                             s, DS);
   }
   __device__ void advance() {}
   template <class Hook>
-  __device__ void scores(floatx16 (&sc)[SH::KB], const uint8_t* lds, int l32, int hl, Hook&& hook) const {
+  __device__ void scores(typename Layout::Scores& sc, const uint8_t* lds, int lane, Hook&& hook) const {
     const uint16_t* k_lds = reinterpret_cast<const uint16_t*>(lds);
+    const int l16 = lane & 15, lq = lane >> 4;
 #pragma unroll
-    for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
-    bf16x8 ka[2][SH::KB];
+    for (int i = 0; i < NR; ++i)
 #pragma unroll
-    for (int kb = 0; kb < SH::KB; ++kb) ka[0][kb] = read_k<SH>(k_lds, kb, 0, l32, hl);
+      for (int kb = 0; kb < KB; ++kb) sc[i][kb] = floatx4{};
+    bf16x8 ka[KB];
 #pragma unroll
-    for (int s = 0; s < SH::DS; ++s) {
+    for (int kb = 0; kb < KB; ++kb) ka[kb] = read_k16<SH>(k_lds, kb, 0, l16, lq);
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
       hook(s);
-      if (s + 1 < SH::DS) {
 #pragma unroll
-        for (int kb = 0; kb < SH::KB; ++kb) ka[(s + 1) & 1][kb] = read_k<SH>(k_lds, kb, s + 1, l32, hl);
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 a = ka[kb];
+        if (s + 1 < DS) ka[kb] = read_k16<SH>(k_lds, kb, s + 1, l16, lq);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) sc[i][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i][s], sc[i][kb], 0, 0, 0);
       }
-#pragma unroll
-      for (int kb = 0; kb < SH::KB; ++kb)
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s & 1][kb], qf[s], sc[kb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -419,15 +560,20 @@ struct QkBf16 {
 template <int D, int BLK>
 struct QkFp8 {
   using SH = Shape8<D, BLK>;
+  using Layout = L32<BLK>;
+  static constexpr int NR = Layout::NR;
   static constexpr int LDS_BYTES = BLK * D;
   const uint8_t* kbase;
   uint32_t bytes;
   int64_t stride;
   intx8 qf[SH::DS];
 
-  __device__ QkFp8(const LaunchParams& p, const WorkItem& w, int64_t head_off, int qrow, bool qvalid, int hl)
+  __device__ QkFp8(const LaunchParams& p, const WorkItem& w, int64_t head_off, const int (&qrows)[NR],
+                   const bool (&qvalids)[NR], int lane)
       : kbase(reinterpret_cast<const uint8_t*>(p.k) + head_off), bytes(head_extent8<D>(w.S, p.stride_tok)),
         stride(p.stride_tok) {
+    const int qrow = qrows[0], hl = lane >> 5;
+    const bool qvalid = qvalids[0];
     // B operand: query qrow, d bytes [64 s + 32 hl, +32)
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + head_off + (int64_t)(qvalid ? qrow : 0) * p.stride_tok +
                         32 * hl;
@@ -449,7 +595,8 @@ struct QkFp8 {
   }
   __device__ void advance() {}
   template <class Hook>
-  __device__ void scores(floatx16 (&sc)[SH::KB], const uint8_t* k_lds, int l32, int hl, Hook&& hook) const {
+  __device__ void scores(typename Layout::Scores& sc, const uint8_t* k_lds, int lane, Hook&& hook) const {
+    const int l32 = lane & 31, hl = lane >> 5;
 #pragma unroll
     for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
 #pragma unroll
@@ -471,6 +618,8 @@ struct QkFp8 {
 template <int D, int BLK>
 struct QkMx {
   using SH = Shape8<D, BLK>;
+  using Layout = L32<BLK>;
+  static constexpr int NR = Layout::NR;
   static constexpr int LDS_BYTES = BLK * D;
   const uint8_t* kbase;
   uint32_t bytes;
@@ -482,9 +631,12 @@ struct QkMx {
   uint32_t ks[SH::KB];     // scale rows of this lane's keys in the K tile in use
   uint32_t ks_nx[SH::KB];  // the same for the next tile when it is fetched during this one
 
-  __device__ QkMx(const LaunchParams& p, const WorkItem& w, int64_t head_off, int qrow, bool qvalid, int hl)
+  __device__ QkMx(const LaunchParams& p, const WorkItem& w, int64_t head_off, const int (&qrows)[NR],
+                  const bool (&qvalids)[NR], int lane)
       : kbase(reinterpret_cast<const uint8_t*>(p.k) + head_off), bytes(head_extent8<D>(w.S, p.stride_tok)),
         stride(p.stride_tok) {
+    const int qrow = qrows[0], hl = lane >> 5;
+    const bool qvalid = qvalids[0];
     constexpr int SROW = D / 32;  // scale bytes per row
     const int64_t sc_off = (int64_t)w.tok0 * p.bs_tok + (int64_t)w.h * p.bs_head;
     const uint32_t sc_bytes = w.S > 0 ? (uint32_t)((int64_t)(w.S - 1) * p.bs_tok + SROW) : 0u;
@@ -533,7 +685,8 @@ struct QkMx {
     for (int kb = 0; kb < SH::KB; ++kb) ks[kb] = ks_nx[kb];
   }
   template <class Hook>
-  __device__ void scores(floatx16 (&sc)[SH::KB], const uint8_t* k_lds, int l32, int hl, Hook&& hook) const {
+  __device__ void scores(typename Layout::Scores& sc, const uint8_t* k_lds, int lane, Hook&& hook) const {
+    const int l32 = lane & 31, hl = lane >> 5;
 #pragma unroll
     for (int kb = 0; kb < SH::KB; ++kb) sc[kb] = floatx16{};
 #pragma unroll
@@ -550,12 +703,82 @@ struct QkMx {
   }
 };
 
-// bf16 V and P: P rounded to bf16 feeds O^T += V^T P^T directly from the
+// O^T accumulators and the epilogue of each layout: zeroing, the lazy
+// rescale by a per-row factor, and the store of O = acc * inv as bf16.
+// L32: lane l holds query l % 32, d = 32 mb + 8 g + 4 (l / 32) + e in
+// register 4 g + e of block mb.
+template <int D>
+struct AccL32 {
+  static constexpr int NR = 1;
+  static constexpr int MB = D / 32;
+  using Acc = floatx16[MB];
+  __device__ static void zero(Acc& acc) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx16{};
+  }
+  __device__ static void rescale(Acc& acc, const float (&alpha)[NR]) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha[0];
+  }
+  __device__ static void store(const Acc& acc, const float (&inv)[NR], uint16_t* obase, const int (&qrow)[NR],
+                               const bool (&qvalid)[NR], int64_t stride, int lane) {
+    if (!qvalid[0]) return;
+    uint16_t* op = obase + (int64_t)qrow[0] * stride + 4 * (lane >> 5);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const floatx4 f = {acc[mb][4 * g] * inv[0], acc[mb][4 * g + 1] * inv[0], acc[mb][4 * g + 2] * inv[0],
+                           acc[mb][4 * g + 3] * inv[0]};
+        *reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * g) = __builtin_convertvector(f, bf16x4);
+      }
+  }
+};
+
+// L16: lane l holds queries 16 i + l % 16 (i = 0, 1), d = 16 mb + 4 (l / 16) + r
+// in register r of block [i][mb].
+template <int D>
+struct AccL16 {
+  static constexpr int NR = 2;
+  static constexpr int MB = D / 16;
+  using Acc = floatx4[NR][MB];
+  __device__ static void zero(Acc& acc) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[i][mb] = floatx4{};
+  }
+  __device__ static void rescale(Acc& acc, const float (&alpha)[NR]) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[i][mb] *= alpha[i];
+  }
+  __device__ static void store(const Acc& acc, const float (&inv)[NR], uint16_t* obase, const int (&qrow)[NR],
+                               const bool (&qvalid)[NR], int64_t stride, int lane) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      if (!qvalid[i]) continue;
+      uint16_t* op = obase + (int64_t)qrow[i] * stride + 4 * (lane >> 4);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const floatx4 f = acc[i][mb] * inv[i];
+        *reinterpret_cast<bf16x4*>(op + 16 * mb) = __builtin_convertvector(f, bf16x4);
+      }
+    }
+  }
+};
+
+// bf16 V and P in layout L32 (the block-scaled q/k mode's P.V): P rounded to
+// bf16 feeds O^T += V^T P^T (v_mfma_f32_32x32x16_bf16) directly from the
 // score registers; V^T comes from the row-major V tile through transposing
 // LDS reads, two 16-key steps ahead of their MFMAs.
 template <int D, int BLK>
-struct PvBf16 {
+struct PvBf16 : AccL32<D> {
   using SH = Shape<D, BLK>;
+  using Layout = L32<BLK>;
+  using typename AccL32<D>::Acc;
+  static constexpr int NR = Layout::NR;
   static constexpr int LDS_BYTES = BLK * D * 2;
   using PFrag = bf16x8[SH::KS];
   const uint16_t* vbase;
@@ -572,22 +795,23 @@ struct PvBf16 {
   }
   __device__ static float out_scale(const LaunchParams&) { return 1.0f; }
   __device__ void fetch(uint8_t* lds, int j, int wave, int lane) {
-    dma_load<D, BLK, true>(vbase, bytes, reinterpret_cast<uint16_t*>(lds), j * BLK, stride, wave, lane);
+    dma_load<D, BLK, Swz::V>(vbase, bytes, reinterpret_cast<uint16_t*>(lds), j * BLK, stride, wave, lane);
   }
   // P = 2^(s * c2 - m) in the slot order of the P.V B operand; l += row sum
-  __device__ static void make_p(const floatx16 (&sc)[BLK / 32], float c2, float nm, float& l, PFrag& pb) {
+  __device__ static void make_p(const typename Layout::Scores& sc, float c2, const float (&nm)[NR], float (&l)[NR],
+                                PFrag& pb) {
 #pragma unroll
     for (int s = 0; s < SH::KS; ++s) {
       floatx8 e;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        e[r] = fast_exp2(fmaf(sc[s >> 1][8 * (s & 1) + r], c2, nm));
-        l += e[r];
+        e[r] = fast_exp2(fmaf(sc[s >> 1][8 * (s & 1) + r], c2, nm[0]));
+        l[0] += e[r];
       }
       pb[s] = __builtin_convertvector(e, bf16x8);
     }
   }
-  __device__ void accumulate(floatx16 (&acc)[SH::MB], const uint8_t* lds, const PFrag& pb) const {
+  __device__ void accumulate(Acc& acc, const uint8_t* lds, const PFrag& pb) const {
     const uint16_t* v_lds = reinterpret_cast<const uint16_t*>(lds);
     bf16x8 va[3][SH::MB];
 #pragma unroll
@@ -613,8 +837,11 @@ struct PvBf16 {
 // v_cvt_pk_fp8_f32), V^T gathered by transposing byte reads, P.V on the
 // scaled MFMA with unit block scales; O carries scale_v.
 template <int D, int BLK>
-struct PvFp8 {
+struct PvFp8 : AccL32<D> {
   using SH = Shape8<D, BLK>;
+  using Layout = L32<BLK>;
+  using typename AccL32<D>::Acc;
+  static constexpr int NR = Layout::NR;
   static constexpr int LDS_BYTES = BLK * D;
   using PFrag = intx8[SH::KS];
   const uint8_t* vbase;
@@ -641,24 +868,25 @@ struct PvFp8 {
     dma_load8<D, BLK, true>(vbase, bytes, lds, j * BLK, stride, wave, lane);
   }
   // P^T for 64-key step s: byte 16 u + r is score register r of key block 2 s + u
-  __device__ static void make_p(const floatx16 (&sc)[BLK / 32], float c2, float nm, float& l, PFrag& pb) {
+  __device__ static void make_p(const typename Layout::Scores& sc, float c2, const float (&nm)[NR], float (&l)[NR],
+                                PFrag& pb) {
 #pragma unroll
     for (int s = 0; s < SH::KS; ++s)
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int kb = 2 * s + (w >> 2);
         const int r0 = 4 * (w & 3);
-        float e0 = fast_exp2(fmaf(sc[kb][r0], c2, nm));
-        float e1 = fast_exp2(fmaf(sc[kb][r0 + 1], c2, nm));
-        float e2 = fast_exp2(fmaf(sc[kb][r0 + 2], c2, nm));
-        float e3 = fast_exp2(fmaf(sc[kb][r0 + 3], c2, nm));
-        l += (e0 + e1) + (e2 + e3);
+        float e0 = fast_exp2(fmaf(sc[kb][r0], c2, nm[0]));
+        float e1 = fast_exp2(fmaf(sc[kb][r0 + 1], c2, nm[0]));
+        float e2 = fast_exp2(fmaf(sc[kb][r0 + 2], c2, nm[0]));
+        float e3 = fast_exp2(fmaf(sc[kb][r0 + 3], c2, nm[0]));
+        l[0] += (e0 + e1) + (e2 + e3);
         int word = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, word, true);
         pb[s][w] = word;
       }
   }
-  __device__ void accumulate(floatx16 (&acc)[SH::MB], const uint8_t* v_lds, const PFrag& pb) const {
+  __device__ void accumulate(Acc& acc, const uint8_t* v_lds, const PFrag& pb) const {
 #pragma unroll
     for (int s = 0; s < SH::KS; ++s) {
       intx8 va[SH::MB];
@@ -668,6 +896,70 @@ struct PvFp8 {
       for (int mb = 0; mb < SH::MB; ++mb)
         acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[mb], pb[s], acc[mb], 0, 0, 0, kE8M0One, 0,
                                                                   kE8M0One);
+    }
+  }
+};
+
+// bf16 V and P on v_mfma_f32_16x16x32_bf16 (layout L16): P rounded to bf16
+// feeds O^T += V^T P^T from the score registers, slots 0-3 from 16-key block
+// 2 ks and slots 4-7 from block 2 ks + 1 of each 32-key step; V^T comes from
+// the row-major V tile through transposing LDS reads one step ahead.
+template <int D, int BLK>
+struct PvBf16x16 : AccL16<D> {
+  using SH = Shape<D, BLK>;
+  using Layout = L16<BLK>;
+  using typename AccL16<D>::Acc;
+  static constexpr int NR = Layout::NR;
+  static constexpr int MB = D / 16;   // 16-wide d blocks
+  static constexpr int KS = BLK / 32;  // 32-key steps
+  static constexpr int LDS_BYTES = BLK * D * 2;
+  using PFrag = bf16x8[NR][KS];
+  const uint16_t* vbase;
+  uint32_t bytes;
+  int64_t stride;
+  int tr_row, tr_col;  // V^T read position: row within the step, element column within the d block
+
+  __device__ PvBf16x16(const LaunchParams& p, const WorkItem& w, int64_t head_off, int lane)
+      : vbase(p.v + head_off), bytes(head_extent<D>(w.S, p.stride_tok)), stride(p.stride_tok) {
+    tr_row = 4 * (lane >> 4) + ((lane & 15) >> 2);
+    tr_col = 4 * (lane & 3);
+  }
+  __device__ static float out_scale(const LaunchParams&) { return 1.0f; }
+  __device__ void fetch(uint8_t* lds, int j, int wave, int lane) {
+    dma_load<D, BLK, Swz::V16>(vbase, bytes, reinterpret_cast<uint16_t*>(lds), j * BLK, stride, wave, lane);
+  }
+  // P = 2^(s * c2 - m) in the slot order of the P.V B operand; l += row sum
+  __device__ static void make_p(const typename Layout::Scores& sc, float c2, const float (&nm)[NR], float (&l)[NR],
+                                PFrag& pb) {
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        floatx8 e;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          e[r] = fast_exp2(fmaf(sc[i][2 * ks + (r >> 2)][r & 3], c2, nm[i]));
+          l[i] += e[r];
+        }
+        pb[i][ks] = __builtin_convertvector(e, bf16x8);
+      }
+  }
+  __device__ void accumulate(Acc& acc, const uint8_t* lds, const PFrag& pb) const {
+    const uint16_t* v_lds = reinterpret_cast<const uint16_t*>(lds);
+    bf16x8 va[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) va[mb] = read_vt16<SH>(v_lds, 0, mb, tr_row, tr_col);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 a = va[mb];
+        if (ks + 1 < KS) va[mb] = read_vt16<SH>(v_lds, ks + 1, mb, tr_row, tr_col);
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+          acc[i][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[i][ks], acc[i][mb], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 };
@@ -697,9 +989,10 @@ struct Buffering {
 
 template <int D, int BLK, class QK, class PV, bool CALIB>
 __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {  // 2*BLK = 64 * BLK / 32 threads
+  using LY = typename QK::Layout;
+  static_assert(__is_same(LY, typename PV::Layout), "the QK and PV policies must share the score layout");
+  constexpr int NR = LY::NR;    // query rows per lane
   constexpr int NW = BLK / 32;  // waves, 32 query rows each
-  constexpr int KB = BLK / 32;  // 32-key blocks of S^T
-  constexpr int MB = D / 32;    // 32-wide d blocks of O^T
   constexpr bool kDoubleK = Buffering<QK, PV, CALIB>::kDoubleK;
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds[QK::LDS_BYTES];
   __shared__ alignas(Buffering<QK, PV, CALIB>::K1_ALIGN) uint8_t k_lds1[Buffering<QK, PV, CALIB>::K1_BYTES];
@@ -710,17 +1003,21 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps tile addressing scalar
   const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hl = lane >> 5;
 
   const WorkItem w = map_workgroup(p, blockIdx.x, BLK);
   const int b = w.b, h = w.h, qb = w.qb, nK = w.nk, S = w.S;
   const int H = p.num_heads;
   const int64_t head_off = (int64_t)w.tok0 * p.stride_tok + (int64_t)h * p.stride_head;  // elements
 
-  const int qrow = qb * BLK + wave * 32 + l32;
-  const bool qvalid = qrow < S;
-  QK qk(p, w, head_off, qrow, qvalid, hl);
+  int qloc[NR], qrow[NR];  // this lane's rows: within the wave's 32, and within the sequence
+  bool qvalid[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    qloc[i] = LY::row(i, lane);
+    qrow[i] = qb * BLK + wave * 32 + qloc[i];
+    qvalid[i] = qrow[i] < S;
+  }
+  QK qk(p, w, head_off, qrow, qvalid, lane);
   qk.fetch(k_lds, 0, wave, lane);
   PV pv(p, w, head_off, lane);
 
@@ -730,12 +1027,15 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
   const float my_t = (CALIB && lane < ncal) ? p.cal_t[lane] : INFINITY;  // lane k holds threshold k
   int ncount = 0;
 
-  float m_true = -INFINITY;  // running max of the method (log2 units), updated on kept tiles
-  float m_use = -INFINITY;   // exponent base, m_use <= m_true < m_use + slack
-  float l = 0.0f;            // partial row sum over this lane's keys
-  floatx16 acc[MB];
+  float m_true[NR], m_use[NR], l[NR];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx16{};
+  for (int i = 0; i < NR; ++i) {
+    m_true[i] = -INFINITY;  // running max of the method (log2 units), updated on kept tiles
+    m_use[i] = -INFINITY;   // exponent base, m_use <= m_true < m_use + slack
+    l[i] = 0.0f;            // partial row sum over this lane's keys
+  }
+  typename PV::Acc acc;
+  PV::zero(acc);
   int skipped = 0;
 
   wait_dma();
@@ -749,39 +1049,36 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
     const int nvalid = min(BLK, S - j * BLK);
 
     // ---- S^T = K_j Q^T (always paid) -------------------------------------
-    floatx16 sc[KB];
-    qk.scores(sc, kcur, l32, hl, [&](int s) __attribute__((always_inline)) {
+    typename LY::Scores sc;
+    qk.scores(sc, kcur, lane, [&](int s) __attribute__((always_inline)) {
       if constexpr (kDoubleK) qk.fetch_part(knext, j + 1, wave, lane, s, j + 1 < nK);
     });
     if constexpr (kDoubleK) qk.advance();
-    // keys past the sequence end; causal: keys after this lane's query (diagonal tile)
-    const int kmax = (p.causal && j == qb) ? min(nvalid, wave * 32 + l32 + 1) : nvalid;
+    // keys past the sequence end; causal: keys after each row's query (diagonal tile)
     if (p.causal ? j == qb : nvalid < BLK) {
+      int kmax[NR];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (key >= kmax) sc[kb][r] = -INFINITY;
-        }
+      for (int i = 0; i < NR; ++i) kmax[i] = (p.causal && j == qb) ? min(nvalid, wave * 32 + qloc[i] + 1) : nvalid;
+      LY::mask(sc, lane, kmax);
     }
 
     // ---- tile row max and the skip vote ----------------------------------
-    float mx = -INFINITY;
+    float tmax[NR], rowmax[NR], x[NR];
+    LY::row_max(sc, tmax);
+    float xw = -INFINITY;  // this lane's largest margin over its valid rows
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    float rowmax, x;
-    tile_margin(xhalf_max(mx), c2, m_true, rowmax, x);  // m_true = -inf gives x = +inf
-    if (!qvalid) x = -INFINITY;
+    for (int i = 0; i < NR; ++i) {
+      tile_margin(tmax[i], c2, m_true[i], rowmax[i], x[i]);  // m_true = -inf gives x = +inf
+      if (!qvalid[i]) x[i] = -INFINITY;
+      xw = fmaxf(xw, x[i]);
+    }
     bool wait_k = false;
     if constexpr (CALIB) {
       // d = max over valid rows; "some row has x >= t_k" is exactly d >= t_k
-      const float dw = wave_max(x);
+      const float dw = wave_max(xw);
       if (lane == 0) dvote[wave] = dw;
     } else {
-      const bool kw = wave_any(x >= t);
+      const bool kw = wave_any(xw >= t);
       if (lane == 0) vote[wave] = kw ? 1ull : 0ull;
       // A wave that keeps the tile knows it is kept and waits for its share of
       // K_{j+1} with V_j, before the second barrier. The others wait now, so
@@ -814,16 +1111,27 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
       pv.fetch(v_lds, j, wave, lane);
 
       // ---- online softmax (log2 domain), overlapping the V fetch ---------
-      m_true = fmaxf(m_true, rowmax);
-      if (wave_any(rowmax > m_use + kRescaleSlack)) {
-        const float m_new = fmaxf(m_use, rowmax);
-        const float alpha = fast_exp2(m_use - m_new);  // 0 when m_use was -inf
-        l *= alpha;
+      bool up = false;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
-        m_use = m_new;
+      for (int i = 0; i < NR; ++i) {
+        m_true[i] = fmaxf(m_true[i], rowmax[i]);
+        up = up || rowmax[i] > m_use[i] + kRescaleSlack;
       }
-      PV::make_p(sc, c2, -m_use, l, pb);
+      if (wave_any(up)) {
+        float alpha[NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+          const float m_new = fmaxf(m_use[i], rowmax[i]);
+          alpha[i] = fast_exp2(m_use[i] - m_new);  // 0 when m_use was -inf
+          l[i] *= alpha[i];
+          m_use[i] = m_new;
+        }
+        PV::rescale(acc, alpha);
+      }
+      float nm[NR];
+#pragma unroll
+      for (int i = 0; i < NR; ++i) nm[i] = -m_use[i];
+      PV::make_p(sc, c2, nm, l, pb);
     }
     if (!kDoubleK || keep) {
       wait_dma();
@@ -844,19 +1152,10 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
   }
 
   // ---- epilogue ---------------------------------------------------------
-  const float inv = PV::out_scale(p) / xhalf_sum(l);
-  if (qvalid) {
-    uint16_t* op = p.o + head_off + (int64_t)qrow * p.stride_tok;
+  float inv[NR];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const floatx4 f = {acc[mb][4 * g] * inv, acc[mb][4 * g + 1] * inv, acc[mb][4 * g + 2] * inv,
-                           acc[mb][4 * g + 3] * inv};
-        const bf16x4 o4 = __builtin_convertvector(f, bf16x4);
-        *reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * g + 4 * hl) = o4;
-      }
-  }
+  for (int i = 0; i < NR; ++i) inv[i] = PV::out_scale(p) / LY::row_sum(l[i]);
+  PV::store(acc, inv, p.o + head_off, qrow, qvalid, p.stride_tok, lane);
   if constexpr (CALIB) {
     if (wave == 0 && lane < ncal) p.counts[(p.wg_abs0 + w.row) * ncal + lane] = ncount;
     if (tid == 0) p.tiles[p.wg_abs0 + w.row] = nK;
@@ -887,7 +1186,7 @@ int launch(const LaunchParams& p, hipStream_t stream) {
   } else if (p.mxqk) {
     hipLaunchKernelGGL((fwd_kernel<D, BLK, QkMx<D, BLK>, PvBf16<D, BLK>, CALIB>), grid, threads, 0, stream, p);
   } else {
-    hipLaunchKernelGGL((fwd_kernel<D, BLK, QkBf16<D, BLK>, PvBf16<D, BLK>, CALIB>), grid, threads, 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, BLK, QkBf16<D, BLK>, PvBf16x16<D, BLK>, CALIB>), grid, threads, 0, stream, p);
   }
   return (int)hipGetLastError();
 }
