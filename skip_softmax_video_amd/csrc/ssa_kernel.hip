@@ -194,12 +194,17 @@ __device__ __forceinline__ float xrow_sum(float x) {
 }
 
 // A operand of the 16x16x32 S^T = K Q^T for 16-key block kb, 32-wide d
-// step s: K[16 kb + l16][32 s + 8 lq .. + 7] (l16 = l % 16, lq = l / 16)
+// step s: K[16 kb + l16][32 s + 8 lq .. + 7] (l16 = l % 16, lq = l / 16).
+// The K swizzle of row 16 kb + l16 is l16 (it repeats every 16 rows), so
+// k16_off(s) serves every key block: block kb adds 16 rows (an immediate).
 template <class SH>
-__device__ __forceinline__ bf16x8 read_k16(const uint16_t* k_lds, int kb, int s, int l16, int lq) {
-  const int row = 16 * kb + l16;
-  const int gran = row * SH::CH + ((4 * s + lq) ^ swz_k<SH::CH>(row));
-  return *reinterpret_cast<const bf16x8*>(k_lds + gran * 8);
+__device__ __forceinline__ uint32_t k16_off(int s, int lane) {
+  const int l16 = lane & 15, lq = lane >> 4;
+  return (uint32_t)((l16 * SH::CH + ((4 * s + lq) ^ swz_k<SH::CH>(l16))) * 16);
+}
+template <class SH>
+__device__ __forceinline__ bf16x8 read_k16(const uint8_t* k_lds, int kb, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(k_lds + off + kb * 16 * SH::CH * 16);
 }
 
 // A operand of the 16x16x32 O^T += V^T P^T for 32-key step ks, 16-wide d
@@ -207,16 +212,22 @@ __device__ __forceinline__ bf16x8 read_k16(const uint16_t* k_lds, int kb, int s,
 // (slots 0-3) and 32 ks + 16 + 4 lq + (0..3) (slots 4-7), the key order of
 // P's slots. Each transposing read covers 4 rows x 16 columns per 16 lanes:
 // source lane i names row i / 4 and columns 4 (i % 4) .. + 3, and lane j
-// receives column j; voff holds this lane's row-in-group and column part.
+// receives column j. vt16_off gives this lane's byte offset for d block mb
+// at ks = 0; the row swizzle repeats every 8 rows, so the second read and
+// later steps are that offset plus constants (which the LDS instructions
+// take as immediates).
 template <class SH>
-__device__ __forceinline__ bf16x8 read_vt16(const uint16_t* v_lds, int ks, int mb, int tr_row, int tr_col) {
-  const int r_lo = 32 * ks + tr_row;
-  const int r_hi = r_lo + 16;
-  const int c = 16 * mb + tr_col;  // element column, a multiple of 4
-  const uint16_t* lo = v_lds + (r_lo * SH::CH + ((c >> 3) ^ swz_v16<SH::CH>(r_lo))) * 8 + (c & 7);
-  const uint16_t* hi = v_lds + (r_hi * SH::CH + ((c >> 3) ^ swz_v16<SH::CH>(r_hi))) * 8 + (c & 7);
+__device__ __forceinline__ uint32_t vt16_off(int mb, int lane) {
+  const int row = 4 * (lane >> 4) + ((lane & 15) >> 2);
+  const int col = 16 * mb + 4 * (lane & 3);  // element column, a multiple of 4
+  return (uint32_t)(((row * SH::CH + ((col >> 3) ^ swz_v16<SH::CH>(row))) * 8 + (col & 7)) * 2);
+}
+template <class SH>
+__device__ __forceinline__ bf16x8 read_vt16(const uint8_t* v_lds, int ks, uint32_t off) {
+  constexpr uint32_t kRow = SH::CH * 16;  // bytes per V row
+  const uint8_t* lo = v_lds + off + 32 * ks * kRow;
   const shortx4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)lo);
-  const shortx4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)hi);
+  const shortx4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(lo + 16 * kRow));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -531,22 +542,23 @@ struct QkBf16 {
   __device__ void advance() {}
   template <class Hook>
   __device__ void scores(typename Layout::Scores& sc, const uint8_t* lds, int lane, Hook&& hook) const {
-    const uint16_t* k_lds = reinterpret_cast<const uint16_t*>(lds);
-    const int l16 = lane & 15, lq = lane >> 4;
 #pragma unroll
     for (int i = 0; i < NR; ++i)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sc[i][kb] = floatx4{};
+    uint32_t koff[DS];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) koff[s] = k16_off<SH>(s, lane);
     bf16x8 ka[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) ka[kb] = read_k16<SH>(k_lds, kb, 0, l16, lq);
+    for (int kb = 0; kb < KB; ++kb) ka[kb] = read_k16<SH>(lds, kb, koff[0]);
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       hook(s);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const bf16x8 a = ka[kb];
-        if (s + 1 < DS) ka[kb] = read_k16<SH>(k_lds, kb, s + 1, l16, lq);
+        if (s + 1 < DS) ka[kb] = read_k16<SH>(lds, kb, koff[s + 1]);
 #pragma unroll
         for (int i = 0; i < NR; ++i) sc[i][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[i][s], sc[i][kb], 0, 0, 0);
       }
@@ -917,12 +929,12 @@ struct PvBf16x16 : AccL16<D> {
   const uint16_t* vbase;
   uint32_t bytes;
   int64_t stride;
-  int tr_row, tr_col;  // V^T read position: row within the step, element column within the d block
+  uint32_t voff[MB];  // V^T read offsets (bytes, ks = 0) of this lane per d block
 
   __device__ PvBf16x16(const LaunchParams& p, const WorkItem& w, int64_t head_off, int lane)
       : vbase(p.v + head_off), bytes(head_extent<D>(w.S, p.stride_tok)), stride(p.stride_tok) {
-    tr_row = 4 * (lane >> 4) + ((lane & 15) >> 2);
-    tr_col = 4 * (lane & 3);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) voff[mb] = vt16_off<SH>(mb, lane);
   }
   __device__ static float out_scale(const LaunchParams&) { return 1.0f; }
   __device__ void fetch(uint8_t* lds, int j, int wave, int lane) {
@@ -945,16 +957,15 @@ struct PvBf16x16 : AccL16<D> {
       }
   }
   __device__ void accumulate(Acc& acc, const uint8_t* lds, const PFrag& pb) const {
-    const uint16_t* v_lds = reinterpret_cast<const uint16_t*>(lds);
     bf16x8 va[MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) va[mb] = read_vt16<SH>(v_lds, 0, mb, tr_row, tr_col);
+    for (int mb = 0; mb < MB; ++mb) va[mb] = read_vt16<SH>(lds, 0, voff[mb]);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const bf16x8 a = va[mb];
-        if (ks + 1 < KS) va[mb] = read_vt16<SH>(v_lds, ks + 1, mb, tr_row, tr_col);
+        if (ks + 1 < KS) va[mb] = read_vt16<SH>(lds, ks + 1, voff[mb]);
 #pragma unroll
         for (int i = 0; i < NR; ++i)
           acc[i][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[i][ks], acc[i][mb], 0, 0, 0);
@@ -977,13 +988,18 @@ struct PvBf16x16 : AccL16<D> {
 //     and waited for its share of K_{j+1} before it); a kept tile adds the V
 //     fetch and a second barrier before P.V, after which both tiles are in.
 //   * single K otherwise (bf16 with head_dim 128 and 128-row tiles, where K
-//     and V take 32 KB each): K_{j+1} is fetched after the vote, once every
-//     wave is done reading K_j, and every tile ends with a wait and a barrier.
+//     and V take 32 KB each, and every calibration pass): K_{j+1} is fetched
+//     after the vote, once every wave is done reading K_j, and every tile
+//     ends with a wait and a barrier.
+// With one barrier per skipped tile a fast wave can reach the next tile's
+// vote before a slow one has read this tile's, so the vote slots alternate
+// by tile parity (the slot of tile j is rewritten at tile j + 2, after a
+// barrier every wave passes only once it has read tile j's votes).
 // ===========================================================================
 template <class QK, class PV, bool CALIB>
 struct Buffering {
   static constexpr bool kDoubleK = !CALIB && 2 * QK::LDS_BYTES + PV::LDS_BYTES <= 64 * 1024;
-  static constexpr int K1_BYTES = kDoubleK ? QK::LDS_BYTES : 16;  // unused in the single-K scheme
+  static constexpr int K1_BYTES = kDoubleK ? QK::LDS_BYTES : 16;  // unused in the other schemes
   static constexpr int K1_ALIGN = kDoubleK ? 1024 : 16;
 };
 
@@ -997,8 +1013,8 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds[QK::LDS_BYTES];
   __shared__ alignas(Buffering<QK, PV, CALIB>::K1_ALIGN) uint8_t k_lds1[Buffering<QK, PV, CALIB>::K1_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds[PV::LDS_BYTES];
-  __shared__ uint64_t vote[NW];
-  __shared__ float dvote[NW];  // calibration: each wave's maximum of x
+  __shared__ uint64_t vote[2][NW];  // by tile parity
+  __shared__ float dvote[2][NW];    // calibration: each wave's maximum of x
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps tile addressing scalar
@@ -1047,13 +1063,19 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
   // depend on the copy into knext and adds no wait for it.
   auto tile = [&](uint8_t* kcur, uint8_t* knext, const int j) __attribute__((always_inline)) {
     const int nvalid = min(BLK, S - j * BLK);
+    const bool more = j + 1 < nK;
+    constexpr bool pf = kDoubleK;  // K_{j+1} streams into knext during this tile's S^T
 
     // ---- S^T = K_j Q^T (always paid) -------------------------------------
     typename LY::Scores sc;
-    qk.scores(sc, kcur, lane, [&](int s) __attribute__((always_inline)) {
-      if constexpr (kDoubleK) qk.fetch_part(knext, j + 1, wave, lane, s, j + 1 < nK);
-    });
-    if constexpr (kDoubleK) qk.advance();
+    if constexpr (kDoubleK) {
+      qk.scores(sc, kcur, lane, [&](int s) __attribute__((always_inline)) {
+        qk.fetch_part(knext, j + 1, wave, lane, s, more);  // empty range at the last tile
+      });
+      qk.advance();
+    } else {
+      qk.scores(sc, kcur, lane, [](int) {});
+    }
     // keys past the sequence end; causal: keys after each row's query (diagonal tile)
     if (p.causal ? j == qb : nvalid < BLK) {
       int kmax[NR];
@@ -1076,36 +1098,36 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
     if constexpr (CALIB) {
       // d = max over valid rows; "some row has x >= t_k" is exactly d >= t_k
       const float dw = wave_max(xw);
-      if (lane == 0) dvote[wave] = dw;
+      if (lane == 0) dvote[j & 1][wave] = dw;
     } else {
       const bool kw = wave_any(xw >= t);
-      if (lane == 0) vote[wave] = kw ? 1ull : 0ull;
+      if (lane == 0) vote[j & 1][wave] = kw ? 1ull : 0ull;
       // A wave that keeps the tile knows it is kept and waits for its share of
       // K_{j+1} with V_j, before the second barrier. The others wait now, so
       // that when every wave skips, K_{j+1} is complete at this barrier.
-      wait_k = kDoubleK && !kw;
+      wait_k = pf && !kw;
     }
     if (wait_k) wait_dma();
     __syncthreads();  // votes (and K_{j+1}) visible; every wave is done reading K_j and V_{j-1}
 
     bool keep;
     if constexpr (CALIB) {
-      float d = dvote[0];
+      float d = dvote[j & 1][0];
 #pragma unroll
-      for (int v = 1; v < NW; ++v) d = fmaxf(d, dvote[v]);
+      for (int v = 1; v < NW; ++v) d = fmaxf(d, dvote[j & 1][v]);
       ncount += d < my_t ? 1 : 0;  // lanes >= ncal hold +inf and are never written out
       keep = true;
     } else {
-      uint64_t all = vote[0];
+      uint64_t all = vote[j & 1][0];
 #pragma unroll
-      for (int v = 1; v < NW; ++v) all |= vote[v];
+      for (int v = 1; v < NW; ++v) all |= vote[j & 1][v];
       keep = __builtin_amdgcn_readfirstlane(all != 0 ? 1 : 0) != 0;  // work-group uniform
       skipped += keep ? 0 : 1;
       if (p.tile_mask != nullptr && tid == 0)
         p.tile_mask[((int64_t)((p.seq_abs0 + b) * H + h) * p.mask_nq + qb) * p.mask_nk + j] = keep ? 0 : 1;
     }
 
-    if (!kDoubleK && j + 1 < nK) qk.fetch(kcur, j + 1, wave, lane);
+    if (!pf && more) qk.fetch(kcur, j + 1, wave, lane);
     typename PV::PFrag pb;
     if (keep) {
       pv.fetch(v_lds, j, wave, lane);
@@ -1133,9 +1155,9 @@ __global__ __launch_bounds__(2 * BLK, 2) void fwd_kernel(const LaunchParams p) {
       for (int i = 0; i < NR; ++i) nm[i] = -m_use[i];
       PV::make_p(sc, c2, nm, l, pb);
     }
-    if (!kDoubleK || keep) {
+    if (!pf || keep) {
       wait_dma();
-      __syncthreads();  // V_j (and in the single-K scheme K_{j+1} with its scales) visible
+      __syncthreads();  // V_j and K_{j+1} (with its scales) visible
     }
 
     // ---- O^T += V_j^T P^T ------------------------------------------------
