@@ -957,15 +957,19 @@ struct PvBf16x16 : AccL16<D> {
       }
   }
   __device__ void accumulate(Acc& acc, const uint8_t* lds, const PFrag& pb) const {
-    bf16x8 va[MB];
+    // V^T fragments two steps ahead: the first two steps' reads all issue before any MFMA
+    bf16x8 va[2][MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) va[mb] = read_vt16<SH>(lds, 0, voff[mb]);
+    for (int s0 = 0; s0 < 2 && s0 < KS; ++s0)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) va[s0][mb] = read_vt16<SH>(lds, s0, voff[mb]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 a = va[mb];
-        if (ks + 1 < KS) va[mb] = read_vt16<SH>(lds, ks + 1, voff[mb]);
+        const bf16x8 a = va[ks & 1][mb];
+        if (ks + 2 < KS) va[ks & 1][mb] = read_vt16<SH>(lds, ks + 2, voff[mb]);
 #pragma unroll
         for (int i = 0; i < NR; ++i)
           acc[i][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[i][ks], acc[i][mb], 0, 0, 0);
