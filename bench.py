@@ -32,7 +32,7 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA, published
 TARGET_SPARSITY = 0.7
 CALIB_LAMBDAS_N = 16
-KERNEL_SOURCE = os.path.join(ROOT, "skip_softmax_video_amd", "csrc", "ssa_kernel.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "skip_softmax_video_amd", "csrc", n) for n in ("ssa_kernel.hip", "ssa_internal.h")]
 
 # HBM traffic of one calibrated-lambda forward launch at the headline shape,
 # from two rocprofv3 counter passes (FETCH_SIZE, WRITE_SIZE) over
@@ -41,8 +41,7 @@ KERNEL_SOURCE = os.path.join(ROOT, "skip_softmax_video_amd", "csrc", "ssa_kernel
 # Valid only for the kernel code it was taken on (sha256 of the source without
 # comments, below); reported
 # as null once the kernel changes.
-TRAFFIC = {"kernel_sha256": "aec808f9a3f47c2a91af5201b84583e4bfe8868831c92f47bebec01d21330cb7",
-           "fetch_bytes": 223056447374, "write_bytes": 992011504}
+TRAFFIC = {"kernel_sha256": "b61ddaca76d45414a785bed012d366f6911d39723ad21305808c009271013d9a", "fetch_bytes": 365310220453, "write_bytes": 992011920}
 
 
 def log(msg: str) -> None:
@@ -78,10 +77,13 @@ def blas_threads() -> int:
 
 
 def kernel_digest() -> str:
-    """sha256 of the kernel source with // comments and blank lines removed."""
+    """sha256 of the kernel sources (the kernels and the work-group mapping
+    they include) with // comments and blank lines removed."""
     import re
-    with open(KERNEL_SOURCE, "r") as f:
-        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f]
+    lines = []
+    for path in KERNEL_SOURCES:
+        with open(path, "r") as f:
+            lines += [re.sub(r"//.*$", "", ln).rstrip() for ln in f]
     return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
 
 

@@ -64,15 +64,26 @@ struct WorkItem {
 };
 
 // Work-group `bid` of a launch -> its work item. The hardware deals
-// work-group i to XCD i % 8; XCD x takes the logical ids
-// [x * (G / 8) + min(x, G % 8), ...), so each XCD walks consecutive Q-blocks
-// of one head and the K/V tiles they stream share that XCD's L2. Logical ids
-// run sequence-major, then head, then Q-block; in the causal form the
-// longest Q-blocks (most KV tiles) of each head come first.
+// work-group i to XCD i % 8. Logical ids are cut into chunks of kXcdChunk
+// consecutive ids and the chunks are dealt round-robin to the XCDs: XCD x
+// takes chunks x, x + 8, x + 16, ... So the work-groups resident on one XCD
+// are consecutive Q-blocks of one head, streaming the same K/V tiles through
+// that XCD's L2, and at any time the eight XCDs work on neighbouring chunks
+// of the same head, whose K/V the Infinity Cache then serves to all of them.
+// Every XCD also receives a share of every head, which evens out heads of
+// different sparsity when a launch holds few heads. Work-groups past the last
+// whole round of 8 chunks keep their own id. Logical ids run sequence-major,
+// then head, then Q-block; in the causal form the longest Q-blocks (most KV
+// tiles) of each head come first.
+constexpr int kXcdChunk = 32;
 SSA_HOST_DEVICE inline WorkItem map_workgroup(const LaunchParams& p, int bid, int block) {
   const int G = p.total_wg;
-  const int xcd = bid & 7;
-  const int L = xcd * (G >> 3) + (xcd < (G & 7) ? xcd : (G & 7)) + (bid >> 3);
+  const int whole = G / (8 * kXcdChunk) * (8 * kXcdChunk);
+  int L = bid;
+  if (bid < whole) {
+    const int k = bid >> 3;  // this work-group's position within its XCD's stream
+    L = ((k / kXcdChunk) * 8 + (bid & 7)) * kXcdChunk + k % kXcdChunk;
+  }
   WorkItem w;
   w.b = 0;
   while (w.b + 1 < p.nseq && p.wg_start[w.b + 1] <= L) ++w.b;

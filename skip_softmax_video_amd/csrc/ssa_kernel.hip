@@ -53,8 +53,10 @@
 //     into a second K buffer during S^T = K_j Q^T where LDS allows, else as
 //     soon as every wave is done reading K_j (see the tile loop).
 //   * Work-groups are remapped so that each XCD (8 per MI355X, 4 MB L2 each)
-//     receives a contiguous range of Q-blocks of the same head: co-resident
-//     work-groups stream the same K/V tiles through their XCD's L2.
+//     receives runs of 32 consecutive Q-blocks of one head, the runs dealt
+//     round-robin over the XCDs (map_workgroup): co-resident work-groups
+//     stream the same K/V tiles through their XCD's L2, and the eight XCDs
+//     share one head's K/V in the Infinity Cache.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
