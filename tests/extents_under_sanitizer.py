@@ -53,6 +53,8 @@ CASES = [
     ([1, 2, 129], 512, 64, 64),                                 # the head limit
     ([75600, 32760, 8190], 40, 128, 128),                       # the varlen batch
     ([5, 0], 2, 128, 64),                                       # empty last sequence
+    ([75600], 40, 128, 128),                                    # the headline: whole XCD rounds and a tail
+    ([256 * 128 + 1], 1, 64, 128),                              # one work-group past whole rounds of chunks
 ]
 
 
