@@ -372,6 +372,34 @@ def main() -> int:
     log(f"mxfp8 q/k: dense {m_dense_ms:.2f} ms, lambda {lam07:.4g} -> {m_ms:.2f} ms (sparsity {m_sp:.4f})")
     del dm, bsc
 
+    # the WAN-5B-like config (H=24, S=16,384 on a 16x32x32 grid): dense and lambda = 1e-3, skip counts per head
+    wcfg = CONFIGS["wan5b"]
+    log("generating the WAN-5B-like sample")
+    xw = make_inputs(wcfg)
+    dw = upload(xw)
+    cuw = xw["cu_seqlens"]
+    del xw
+    ow = torch.empty_like(dw["q"])
+    skw = torch.zeros(wcfg.num_heads, dtype=torch.int64, device="cuda")
+    ttw = torch.zeros(wcfg.num_heads, dtype=torch.int64, device="cuda")
+    ssa.attn_fwd(dw["q"], dw["k"], dw["v"], cuw, 1e-3, block=wcfg.block, out=ow, skipped=skw, total=ttw)
+    torch.cuda.synchronize()
+    w_head = (skw.double() / ttw.double()).cpu().numpy()
+    w_sp = float(skw.sum()) / float(ttw.sum())
+    wan_fwd = lambda lam: (lambda: ssa.attn_fwd(dw["q"], dw["k"], dw["v"], cuw, lam, block=wcfg.block, out=ow))
+    w_dense_ms = time_launches(wan_fwd(0.0), 1, max(2, args.steps // 2))
+    w_ms = time_launches(wan_fwd(1e-3), 1, max(2, args.steps // 2))
+    wan5b = {"heads": wcfg.num_heads, "seq_len": wcfg.seq_lens[0], "lambda": 1e-3,
+             "achieved_tile_sparsity": round(w_sp, 4), "dense_ms": round(w_dense_ms, 3), "ms": round(w_ms, 3),
+             "speedup_vs_dense": round(w_dense_ms / w_ms, 3),
+             "dense_tflops": round(wcfg.dense_flops() / (w_dense_ms * 1e-3) / 1e12, 2),
+             "tflops_dense_equiv": round(wcfg.dense_flops() / (w_ms * 1e-3) / 1e12, 2),
+             "skipped_tiles_per_head": [int(v) for v in skw.cpu().numpy()],
+             "tiles_per_head": int(ttw[0].item()),
+             "tile_sparsity_per_head": [round(float(v), 4) for v in w_head]}
+    log(f"wan5b: dense {w_dense_ms:.2f} ms, lambda 1e-3 -> {w_ms:.2f} ms (sparsity {w_sp:.4f})")
+    del dw, ow
+
     dense_flops = cfg.dense_flops()
     exec_flops = dense_flops / 2 * (2 - s_ach)
     value = dense_flops / (sparse_ms * 1e-3) / 1e12
@@ -404,6 +432,7 @@ def main() -> int:
         "gating": gating,
         "causal": causal,
         "head_shard_8way": head_shard,
+        "wan5b": wan5b,
         "fp8": fp8,
         "mxfp8_qk_bf16_v": block_scaled,
         "calibration": {"pass_ms": round(calib_ms, 3), "fit_resolve_host_ms": round(host_ms, 3),
