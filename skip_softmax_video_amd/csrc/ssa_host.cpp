@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "ssa.h"
@@ -154,6 +155,12 @@ void plan_launches(const ssa_problem* p, const ssa::LaunchParams& tmpl, const st
     }
     lp.nseq = n;
     lp.total_wg = (int32_t)wg;
+    // XCD order (map_workgroup): chunked when eight heads' K/V exceed half the
+    // Infinity Cache or when there are too few heads to balance over 8 XCDs
+    int64_t max_s = 0;
+    for (int i = 0; i < n; ++i) max_s = std::max<int64_t>(max_s, seq_len(p, b0 + i));
+    const int64_t kv_head = max_s * p->head_dim * ((tmpl.fp8 || tmpl.mxqk ? 1 : 2) + (tmpl.fp8 ? 1 : 2));
+    lp.xcd_chunked = (n * H < ssa::kXcdChunkMinHeads || 8 * kv_head > ssa::kXcdChunkKvBytes) ? 1 : 0;
     lp.seq_abs0 = b0;
     lp.wg_abs0 = wg_abs;
     plan->launches.push_back(lp);

@@ -32,6 +32,7 @@ struct LaunchParams {
   int64_t bs_tok, bs_head;                   // mxqk: byte strides of the scale arrays
   int32_t nseq;                              // sequences in this launch
   int32_t total_wg;                          // work-groups in this launch
+  int32_t xcd_chunked;                       // work-group order across XCDs (map_workgroup)
   int32_t seq_abs0;                          // batch index of the first sequence
   int32_t tok_start[kMaxSeqPerLaunch + 1];   // token offset of each sequence (+ end)
   int32_t wg_start[kMaxSeqPerLaunch + 1];    // first work-group of each sequence (+ end)
@@ -64,25 +65,36 @@ struct WorkItem {
 };
 
 // Work-group `bid` of a launch -> its work item. The hardware deals
-// work-group i to XCD i % 8. Logical ids are cut into chunks of kXcdChunk
-// consecutive ids and the chunks are dealt round-robin to the XCDs: XCD x
-// takes chunks x, x + 8, x + 16, ... So the work-groups resident on one XCD
-// are consecutive Q-blocks of one head, streaming the same K/V tiles through
-// that XCD's L2, and at any time the eight XCDs work on neighbouring chunks
-// of the same head, whose K/V the Infinity Cache then serves to all of them.
-// Every XCD also receives a share of every head, which evens out heads of
-// different sparsity when a launch holds few heads. Work-groups past the last
-// whole round of 8 chunks keep their own id. Logical ids run sequence-major,
-// then head, then Q-block; in the causal form the longest Q-blocks (most KV
-// tiles) of each head come first.
+// work-group i to XCD i % 8, and the work-groups resident on one XCD should
+// be consecutive Q-blocks of one head, which stream the same K/V tiles
+// through that XCD's L2. Two orders do that:
+//  * contiguous: XCD x takes the logical ids [x * (G / 8) + min(x, G % 8),
+//    ...), so each XCD walks its own heads and the eight XCDs have eight
+//    heads' K/V in flight;
+//  * chunked (xcd_chunked): logical ids are cut into chunks of kXcdChunk and
+//    the chunks dealt round-robin, XCD x taking chunks x, x + 8, ...; the
+//    eight XCDs then work on neighbouring chunks of the same head, whose K/V
+//    the Infinity Cache serves to all of them, and every XCD gets a share of
+//    every head. Work-groups past the last whole round of 8 chunks keep their
+//    own id.
+// The host picks chunked when eight heads' K/V would not fit in half the
+// Infinity Cache, or when the launch has too few (sequence, head) pairs to
+// balance whole heads over the XCDs; the contiguous order keeps the better
+// L2 hit rate otherwise. Logical ids run sequence-major, then head, then
+// Q-block; in the causal form the longest Q-blocks (most KV tiles) of each
+// head come first.
 constexpr int kXcdChunk = 32;
+constexpr int64_t kXcdChunkKvBytes = 128ll << 20;  // chunked above this much K/V for 8 heads
+constexpr int kXcdChunkMinHeads = 16;              // chunked below this many (sequence, head) pairs
 SSA_HOST_DEVICE inline WorkItem map_workgroup(const LaunchParams& p, int bid, int block) {
   const int G = p.total_wg;
-  const int whole = G / (8 * kXcdChunk) * (8 * kXcdChunk);
-  int L = bid;
-  if (bid < whole) {
-    const int k = bid >> 3;  // this work-group's position within its XCD's stream
-    L = ((k / kXcdChunk) * 8 + (bid & 7)) * kXcdChunk + k % kXcdChunk;
+  const int k = bid >> 3, xcd = bid & 7;  // the XCD and this work-group's position in its stream
+  int L;
+  if (p.xcd_chunked) {
+    const int whole = G / (8 * kXcdChunk) * (8 * kXcdChunk);
+    L = bid < whole ? ((k / kXcdChunk) * 8 + xcd) * kXcdChunk + k % kXcdChunk : bid;
+  } else {
+    L = xcd * (G >> 3) + (xcd < (G & 7) ? xcd : (G & 7)) + k;
   }
   WorkItem w;
   w.b = 0;

@@ -52,11 +52,12 @@
 //     the vote so that it lands while the softmax runs; K_{j+1} is fetched
 //     into a second K buffer during S^T = K_j Q^T where LDS allows, else as
 //     soon as every wave is done reading K_j (see the tile loop).
-//   * Work-groups are remapped so that each XCD (8 per MI355X, 4 MB L2 each)
-//     receives runs of 32 consecutive Q-blocks of one head, the runs dealt
-//     round-robin over the XCDs (map_workgroup): co-resident work-groups
-//     stream the same K/V tiles through their XCD's L2, and the eight XCDs
-//     share one head's K/V in the Infinity Cache.
+//   * Work-groups are remapped so that the ones resident on an XCD (8 per
+//     MI355X, 4 MB L2 each) are consecutive Q-blocks of one head and stream
+//     the same K/V tiles through that XCD's L2 (map_workgroup: each XCD its
+//     own range of heads, or, when eight heads' K/V would overflow the
+//     Infinity Cache, runs of 32 Q-blocks dealt round-robin so that the
+//     eight XCDs share one head's K/V there).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
